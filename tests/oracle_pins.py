@@ -1,0 +1,322 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each ``check_*`` function takes a loaded oracle library handle and raises
+AssertionError when the oracle disagrees with:
+  - exact rational arithmetic (``fractions.Fraction``) on tiny GEMMs,
+  - closed forms (identity B gives C = epilogue(A); all-ones gives C = K),
+  - numpy's binary64 matmul and conversions, torch's exact bf16 widening,
+  - the IEEE round-to-nearest-even definition at constructed midpoints,
+  - high-precision SiLU from mpmath.
+
+The functions are shared by ``test_oracle.py`` (they must pass on the real
+oracle) and by the planted-mistake test (each mutant must fail one of them).
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+
+DTYPES = ("f32", "f16", "bf16")
+EPIS = ("identity", "relu", "silu")
+
+
+# ------------------------------------------------------------------ helpers
+
+def _random_bits(rng, dtype, shape, scale=1.0):
+    """Random finite values of dtype as stored bits (drawn here, not by the oracle)."""
+    x = rng.standard_normal(size=shape) * scale
+    if dtype == "f32":
+        return x.astype(np.float32)
+    if dtype == "f16":
+        return x.astype(np.float16).view(np.uint16)
+    # bf16: truncate a float32 pattern (any bf16 value is a valid input)
+    return (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _exact_values(bits, dtype):
+    """Exact rational value of every stored element, independent of the oracle."""
+    if dtype == "f32":
+        vals = bits.astype(np.float64)
+    elif dtype == "f16":
+        vals = bits.view(np.float16).astype(np.float64)
+    else:
+        vals = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return vals
+
+
+def _frac_gemm(Av, Bv):
+    L, M, K = Av.shape
+    N = Bv.shape[1]
+    out = [[[Fraction(0)] * N for _ in range(M)] for _ in range(L)]
+    mag = [[[Fraction(0)] * N for _ in range(M)] for _ in range(L)]
+    for l in range(L):
+        for m in range(M):
+            for n in range(N):
+                s = Fraction(0)
+                a = Fraction(0)
+                for k in range(K):
+                    p = Fraction(float(Av[l, m, k])) * Fraction(float(Bv[l, n, k]))
+                    s += p
+                    a += abs(p)
+                out[l][m][n] = s
+                mag[l][m][n] = a
+    return out, mag
+
+
+def _silu_mp(x):
+    import mpmath
+
+    mpmath.mp.prec = 200
+    xv = mpmath.mpf(x) if not isinstance(x, Fraction) else mpmath.mpf(x.numerator) / x.denominator
+    return float(xv / (1 + mpmath.exp(-xv)))
+
+
+def _relu_exact(x):
+    return x if x > 0 else 0
+
+
+# ------------------------------------------------------------------ conversions
+
+def check_widen_f16_exhaustive(lib):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.widen(bits, "f16", lib)
+    want = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan), "f16 widen: NaN pattern"
+    assert np.array_equal(got[~nan], want[~nan]), "f16 widen differs from numpy"
+    # sign of zero
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan])), "f16 widen: sign"
+
+
+def check_widen_bf16_exhaustive(lib):
+    import torch
+
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.widen(bits, "bf16", lib)
+    want = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan), "bf16 widen: NaN pattern"
+    assert np.array_equal(got[~nan], want[~nan]), "bf16 widen differs from torch"
+
+
+def _consecutive_midpoints(vals):
+    """For sorted finite positive values v: midpoints (v_i + v_{i+1}) / 2 (exact in fp64)."""
+    lo, hi = vals[:-1], vals[1:]
+    return lo, hi, (lo + hi) / 2.0
+
+
+def check_round_bf16_midpoints(lib):
+    # every finite positive bf16 value, ascending (bit patterns 0x0000 .. 0x7f7f)
+    pos_bits = np.arange(0, 0x7F80, dtype=np.uint32)
+    vals = (pos_bits << 16).view(np.float32).astype(np.float64)
+    # values are fixed points of the rounding
+    got = oracle.round_to_dtype(vals, "bf16", lib)
+    assert np.array_equal(got.astype(np.uint32), pos_bits), "bf16 rounding moves exact values"
+    got = oracle.round_to_dtype(-vals[1:], "bf16", lib)
+    assert np.array_equal(got.astype(np.uint32), pos_bits[1:] | 0x8000), "bf16 negative values"
+    lo, hi, mid = _consecutive_midpoints(vals)
+    lo_b, hi_b = pos_bits[:-1], pos_bits[1:]
+    even = np.where(lo_b % 2 == 0, lo_b, hi_b)
+    got = oracle.round_to_dtype(mid, "bf16", lib).astype(np.uint32)
+    assert np.array_equal(got, even), "bf16 ties must go to even"
+    up = np.nextafter(mid, np.inf)
+    dn = np.nextafter(mid, -np.inf)
+    assert np.array_equal(oracle.round_to_dtype(up, "bf16", lib).astype(np.uint32), hi_b), "bf16 above midpoint"
+    assert np.array_equal(oracle.round_to_dtype(dn, "bf16", lib).astype(np.uint32), lo_b), "bf16 below midpoint"
+    # overflow: the midpoint between the largest finite value and 2^128 is a tie -> inf
+    big = float((2 - 2.0 ** -7) * 2.0 ** 127)
+    edge = float((2 - 2.0 ** -8) * 2.0 ** 127)
+    got = oracle.round_to_dtype(np.array([big, np.nextafter(edge, 0), edge, -edge]), "bf16", lib)
+    assert list(got) == [0x7F7F, 0x7F7F, 0x7F80, 0xFF80], "bf16 overflow threshold"
+    # a value that double rounding through binary32 gets wrong
+    x = 1.0 + 2.0 ** -8 + 2.0 ** -30
+    assert int(oracle.round_to_dtype(np.array([x]), "bf16", lib)[0]) == 0x3F81, "bf16 single rounding"
+
+
+def check_round_f16_vs_numpy(lib):
+    rng = np.random.default_rng(7)
+    # random magnitudes over the whole fp16 range, subnormals and overflow included
+    x = np.ldexp(rng.uniform(1.0, 2.0, 200000), rng.integers(-30, 18, 200000))
+    x *= np.where(rng.integers(0, 2, x.size) == 1, -1.0, 1.0)
+    want = x.astype(np.float16).view(np.uint16)
+    got = oracle.round_to_dtype(x, "f16", lib)
+    assert np.array_equal(got, want), "f16 rounding differs from numpy on random values"
+    # midpoints between consecutive fp16 values, and one binary64 ulp to each side
+    pos_bits = np.arange(0, 0x7C00, dtype=np.uint16)
+    vals = pos_bits.view(np.float16).astype(np.float64)
+    lo, hi, mid = _consecutive_midpoints(vals)
+    for probe in (mid, np.nextafter(mid, np.inf), np.nextafter(mid, -np.inf)):
+        want = probe.astype(np.float16).view(np.uint16)
+        got = oracle.round_to_dtype(probe, "f16", lib)
+        assert np.array_equal(got, want), "f16 rounding differs from numpy near midpoints"
+    lo_b = pos_bits[:-1].astype(np.uint32)
+    hi_b = pos_bits[1:].astype(np.uint32)
+    even = np.where(lo_b % 2 == 0, lo_b, hi_b)
+    assert np.array_equal(oracle.round_to_dtype(mid, "f16", lib).astype(np.uint32), even), "f16 ties to even"
+
+
+def check_round_f32_vs_cast(lib):
+    rng = np.random.default_rng(8)
+    x = np.ldexp(rng.uniform(1.0, 2.0, 200000), rng.integers(-160, 129, 200000))
+    x *= np.where(rng.integers(0, 2, x.size) == 1, -1.0, 1.0)
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float32)
+    got = oracle.round_to_dtype(x, "f32", lib)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), "f32 rounding differs from the binary32 cast"
+
+
+# ------------------------------------------------------------------ epilogues
+
+def check_epilogue_values(lib):
+    ep = lambda x, e: oracle.epilogue64(x, e, lib)  # noqa: E731
+    for x in (-3.5, -1e-300, 0.0, 2.0 ** -1074, 1.0, 7.25, 1e300):
+        assert ep(x, "identity") == x
+        assert ep(x, "relu") == max(x, 0.0)
+    assert math.copysign(1.0, ep(-0.0, "relu")) == 1.0, "relu(-0) must be +0 (where(x > 0, x, 0))"
+    assert ep(0.0, "silu") == 0.0
+    assert ep(1.0, "silu") == 1.0 / (1.0 + math.exp(-1.0))
+    assert ep(1000.0, "silu") == 1000.0
+    v = ep(-1000.0, "silu")
+    assert v == 0.0 and math.copysign(1.0, v) == -1.0, "silu(-1000) is -0"
+    rng = np.random.default_rng(9)
+    for x in np.concatenate([rng.uniform(-40, 40, 300), rng.uniform(-1e-3, 1e-3, 50)]):
+        s = ep(float(x), "silu")
+        ref = _silu_mp(float(x))
+        assert abs(s - ref) <= 4 * np.spacing(abs(ref)) + 1e-300, f"silu({x}) = {s}, want {ref}"
+        # odd-part identity silu(x) - silu(-x) = x
+        d = s - ep(float(-x), "silu")
+        assert abs(d - x) <= 8 * np.spacing(max(abs(x), abs(s))), "silu(x) - silu(-x) = x"
+
+
+# ------------------------------------------------------------------ GEMM pins
+
+def check_closed_form_identity_B(lib):
+    rng = np.random.default_rng(10)
+    for dtype in DTYPES:
+        for epi in EPIS:
+            L, M, K = 2, 9, 13
+            A = _random_bits(rng, dtype, (L, M, K))
+            if dtype == "f32":
+                one, zero = np.float32(1.0), np.float32(0.0)
+                B = np.zeros((L, K, K), np.float32)
+            else:
+                one = np.float16(1.0).view(np.uint16) if dtype == "f16" else np.uint16(0x3F80)
+                zero = np.uint16(0)
+                B = np.full((L, K, K), zero, np.uint16)
+            for l in range(L):
+                np.fill_diagonal(B[l], one)
+            C = oracle.gemm64(A, B, dtype, epi, lib=lib)
+            Av = _exact_values(A, dtype)
+            want = np.vectorize(lambda v: oracle.epilogue64(v, epi, lib))(Av)
+            assert np.array_equal(C, want), f"identity B: C != epi(A) ({dtype}, {epi})"
+            if epi != "silu":
+                bits = oracle.round_to_dtype(C, dtype, lib)
+                if epi == "identity":
+                    assert np.array_equal(bits.view(np.uint8), A.view(np.uint8)), "identity B: bits"
+
+
+def check_closed_form_all_ones(lib):
+    for dtype in DTYPES:
+        for K in (1, 7, 128, 2048):
+            if dtype == "f32":
+                A = np.ones((1, 3, K), np.float32)
+                B = np.ones((1, 5, K), np.float32)
+            else:
+                one = np.float16(1.0).view(np.uint16) if dtype == "f16" else np.uint16(0x3F80)
+                A = np.full((1, 3, K), one, np.uint16)
+                B = np.full((1, 5, K), one, np.uint16)
+            for epi in ("identity", "relu"):
+                C = oracle.gemm64(A, B, dtype, epi, lib=lib)
+                assert np.all(C == float(K)), f"all-ones gives K ({dtype}, K={K})"
+                bits = oracle.round_to_dtype(C, dtype, lib)
+                assert np.all(oracle.widen(bits, dtype, lib) == float(K)), "K is exact in every dtype"
+            C = oracle.gemm64(A, B, dtype, "silu", lib=lib)
+            assert np.allclose(C, K / (1 + math.exp(-K)), rtol=1e-15, atol=0)
+
+
+def check_bruteforce_fraction(lib):
+    rng = np.random.default_rng(11)
+    shapes = [(1, 1, 1, 1), (1, 2, 3, 4), (2, 3, 5, 7), (3, 7, 4, 6), (2, 6, 7, 5), (1, 5, 2, 7)]
+    for dtype in DTYPES:
+        for (L, M, N, K) in shapes:
+            A = _random_bits(rng, dtype, (L, M, K))
+            B = _random_bits(rng, dtype, (L, N, K))
+            exact, mag = _frac_gemm(_exact_values(A, dtype), _exact_values(B, dtype))
+            got = {e: oracle.gemm64(A, B, dtype, e, lib=lib) for e in EPIS}
+            for l in range(L):
+                for m in range(M):
+                    for n in range(N):
+                        s = exact[l][m][n]
+                        bound = K * 2.0 ** -53 * float(mag[l][m][n])
+                        gi = got["identity"][l, m, n]
+                        assert abs(Fraction(gi) - s) <= Fraction(bound), \
+                            f"sum off by more than K*u*sum|ab| ({dtype}, {(L, M, N, K)}, {(l, m, n)})"
+                        gr = got["relu"][l, m, n]
+                        assert gr == max(gi, 0.0) and not (gr == 0 and math.copysign(1, gr) < 0)
+                        assert Fraction(gr) == _relu_exact(Fraction(gi))
+                        ref = _silu_mp(s)
+                        gs = got["silu"][l, m, n]
+                        assert abs(gs - ref) <= 1e-13 * max(abs(ref), 1e-300) + bound * 1.2, \
+                            f"silu of the sum ({dtype}, {(l, m, n)})"
+
+
+def check_matmul_crosscheck(lib):
+    rng = np.random.default_rng(12)
+    for dtype in DTYPES:
+        L, M, N, K = 2, 33, 70, 257
+        A = _random_bits(rng, dtype, (L, M, K))
+        B = _random_bits(rng, dtype, (L, N, K))
+        Av, Bv = _exact_values(A, dtype), _exact_values(B, dtype)
+        ref = np.matmul(Av, np.transpose(Bv, (0, 2, 1)))
+        mag = np.matmul(np.abs(Av), np.transpose(np.abs(Bv), (0, 2, 1)))
+        got = oracle.gemm64(A, B, dtype, "identity", lib=lib)
+        assert np.all(np.abs(got - ref) <= 2 * K * 2.0 ** -53 * mag), f"numpy matmul cross-check ({dtype})"
+        relu = oracle.gemm64(A, B, dtype, "relu", lib=lib)
+        assert np.array_equal(relu, np.where(got > 0, got, 0.0))
+
+
+def check_batch_and_entries(lib):
+    rng = np.random.default_rng(13)
+    for dtype in DTYPES:
+        L, M, N, K = 3, 6, 11, 19
+        A = _random_bits(rng, dtype, (L, M, K))
+        B = _random_bits(rng, dtype, (L, N, K))
+        full = oracle.gemm64(A, B, dtype, "silu", lib=lib)
+        for l in range(L):
+            one = oracle.gemm64(A[l:l + 1], B[l:l + 1], dtype, "silu", lib=lib)
+            assert np.array_equal(one[0], full[l]), "batch independence"
+        li = rng.integers(0, L, 50)
+        mi = rng.integers(0, M, 50)
+        ni = rng.integers(0, N, 50)
+        ent = oracle.gemm_entries64(A, B, dtype, "silu", li, mi, ni, lib=lib)
+        assert np.array_equal(ent, full[li, mi, ni]), "entries agree with the full GEMM"
+
+
+def check_empty_K(lib):
+    for dtype in DTYPES:
+        st = np.float32 if dtype == "f32" else np.uint16
+        A = np.zeros((2, 3, 0), st)
+        B = np.zeros((2, 4, 0), st)
+        for epi in EPIS:
+            C = oracle.gemm64(A, B, dtype, epi, lib=lib)
+            assert C.shape == (2, 3, 4) and np.all(C == 0.0), "K = 0 gives epilogue(0) = 0"
+
+
+ALL_CHECKS = [
+    check_widen_f16_exhaustive,
+    check_widen_bf16_exhaustive,
+    check_round_bf16_midpoints,
+    check_round_f16_vs_numpy,
+    check_round_f32_vs_cast,
+    check_epilogue_values,
+    check_closed_form_identity_B,
+    check_closed_form_all_ones,
+    check_bruteforce_fraction,
+    check_matmul_crosscheck,
+    check_batch_and_entries,
+    check_empty_K,
+]
