@@ -1,0 +1,192 @@
+#!/usr/bin/env python3
+"""Throughput of the tiled dense GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload KEY]
+
+A step is one call of the C entry point gemm_mkl on the headline workload
+(bf16 GEMM M=512 N=5632 K=2048 L=1, ReLU epilogue), i.e. one pass of the whole
+path (tiling, LDS-staged prefetch ring, MFMA mainloop, fused epilogue; plus the
+split-K reduction when the plan splits K).  Inputs are seeded synthetic
+operands resident in HBM before the timed region starts.
+
+Prints ONE JSON line with the metric, the roofline of the dominant kernel
+(measured with HIP events on the stream the kernels run on) and the CPU
+oracle timed on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}   # dense MFMA, 256 CU x 2.4 GHz
+HBM_GBS = 8000.0
+KERNEL_SOURCES = ["tiled_dense_gemm_mkl_amd/csrc/gemm_kernels.hpp",
+                  "tiled_dense_gemm_mkl_amd/csrc/configs.hpp",
+                  "tiled_dense_gemm_mkl_amd/csrc/gemm_api.hip",
+                  "tiled_dense_gemm_mkl_amd/csrc/inst_bf16.hip",
+                  "tiled_dense_gemm_mkl_amd/csrc/inst_f16.hip",
+                  "tiled_dense_gemm_mkl_amd/csrc/inst_f32.hip"]
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_key: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            d = json.load(f)
+        e = d.get(workload_key)
+        if not e or e.get("source_hash") != source_hash():
+            return None
+        return int(e["bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def cpu_baseline(w, A, B):
+    """The oracle as it stands, on this host's cores: full workload, median of 3."""
+    import oracle
+
+    oracle.load()
+    times = []
+    threads = 0
+    for _ in range(3):
+        t0 = time.perf_counter()
+        y = oracle.gemm64(A, B, w.dtype, w.epilogue)
+        times.append(time.perf_counter() - t0)
+        del y
+    threads = oracle.threads()
+    times.sort()
+    t = times[1]
+    return {
+        "value": round(w.flops / t / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"full workload ({w.M}x{w.N}x{w.K}, L={w.L}), binary64 triple loop, median of 3 runs "
+                  f"({t:.2f} s each)",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "the GEMM is not sharded across GPUs in this build", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import tiled_dense_gemm_mkl_amd as gm
+    from tiled_dense_gemm_mkl_amd import workloads
+
+    key = args.workload or workloads.HEADLINE
+    w = workloads.WORKLOADS[key]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    A, B = workloads.make_inputs(w)
+    a = workloads.storage_to_torch(A, w.dtype).to(dev)
+    b = workloads.storage_to_torch(B, w.dtype).to(dev)
+    c = torch.empty((w.L, w.M, w.N), dtype=a.dtype, device=dev)
+    dcode = gm.DTYPE_CODES[w.dtype]
+    ecode = gm.EPILOGUE_CODES[w.epilogue]
+    plan = gm.get_plan(w.M, w.N, w.K, w.L, dcode, ecode)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    ap_, bp_, cp_ = a.data_ptr(), b.data_ptr(), c.data_ptr()
+
+    def step():
+        st = gm.gemm_mkl(ap_, bp_, cp_, w.M, w.N, w.K, w.L, dcode, ecode, sptr)
+        if st != 0:
+            raise gm.GemmMklError(st, gm.status_string(st))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = start.elapsed_time(end)
+    ms_per_step = wall * 1e3 / args.steps
+    ev_ms_per_launch = ev_ms / args.steps
+
+    value = w.flops / (ms_per_step * 1e-3) / 1e12
+    achieved = w.flops / (ev_ms_per_launch * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    traffic = measured_traffic(key)
+
+    result = {
+        "metric": "GEMM TFLOP/s + % of MFMA peak, bf16 M=512 N=5632 K=2048 ReLU, 1 MI355X",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded; A ~ N(0,1), B ~ N(0,0.02^2) for the headline)",
+        "config": {
+            "workload": w.name,
+            "M": w.M, "N": w.N, "K": w.K, "L": w.L,
+            "epilogue": w.epilogue,
+            "plan": {k: plan[k] for k in ("config_id", "prefetch_stages", "split_k", "grid",
+                                           "block_m", "block_n", "block_k", "threads")},
+            "kernel_config": gm.config_names()[plan["config_id"]] if plan["config_id"] >= 0 else "general",
+        },
+        "pct_of_mfma_peak": round(100.0 * value / peak, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+            "algorithmic_bytes": w.algorithmic_bytes,
+            "launch_us": round(ev_ms_per_launch * 1e3, 3),
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, A, B)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,185 @@
+/*
+ * gemm_mkl.h -- C ABI of the MI355X (gfx950) tiled dense GEMM library.
+ *
+ * Operation (for every l < L, m < M, n < N):
+ *
+ *     C[l][m][n] = epilogue( sum_{k<K} A[l][m][k] * B[l][n][k] )
+ *
+ * The operand modes are those of the persistent dense GEMM kernel on
+ * "深入解析 CUTLASS CuTe DSL 的 JIT 函数参数生成机制" (section 2.3): A has modes
+ * (M,K,L), B has (N,K,L), C has (M,N,L).  The epilogue is an elementwise
+ * function chosen at compile time (same page, section 2.3, and the compile-time
+ * ReLU of section 7 of "CUTLASS CuTe DSL 控制流编程指南"); SiLU is the third.
+ *
+ * Layout: packed, batch outermost, K contiguous.
+ *     A: L*M*K elements, element (l,m,k) at ((l*M + m)*K + k)
+ *     B: L*N*K elements, element (l,n,k) at ((l*N + n)*K + k)
+ *     C: L*M*N elements, element (l,m,n) at ((l*M + m)*N + n)
+ * One dtype covers A, B and C; products are formed in the operand precision
+ * and summed in fp32; the epilogue runs on the fp32 sum, which is then rounded
+ * to the output dtype (round to nearest even).
+ *
+ * Pointers: A, B, C are DEVICE pointers owned by the caller; the library never
+ * allocates, frees or retains them.  C must not overlap A or B.  Each base
+ * pointer must be aligned to its element size; 16-byte aligned pointers with
+ * K*sizeof(element) a multiple of 16 take the fast kernels, anything else a
+ * slower general kernel (same results up to fp32 summation order).
+ *
+ * Stream: `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ * enqueue work and return without synchronising; a kernel fault surfaces at
+ * the caller's next synchronisation.  Calls on different streams may run
+ * concurrently; two calls that share an internal split-K workspace are
+ * serialised by the stream they were issued on (the workspace is per device
+ * and per stream).
+ *
+ * Errors: every argument check happens before any HIP call, so a rejected call
+ * touches no device state and leaves C unchanged.  The return value is one of
+ * the GEMM_MKL_STATUS_* codes below.
+ */
+#ifndef GEMM_MKL_H_
+#define GEMM_MKL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Operand / output dtype (A, B and C share it; accumulation is always fp32). */
+enum {
+    GEMM_MKL_F32 = 0,
+    GEMM_MKL_F16 = 1,
+    GEMM_MKL_BF16 = 2
+};
+
+/* Epilogue applied to the fp32 accumulator before the output conversion. */
+enum {
+    GEMM_MKL_EPI_IDENTITY = 0, /* y = x                                  */
+    GEMM_MKL_EPI_RELU = 1,     /* y = x > 0 ? x : 0  (so -0 becomes +0)   */
+    GEMM_MKL_EPI_SILU = 2      /* y = x * sigmoid(x) = x / (1 + exp(-x)) */
+};
+
+/* Status codes. */
+enum {
+    GEMM_MKL_STATUS_OK = 0,
+    GEMM_MKL_STATUS_INVALID_VALUE = -1,        /* null pointer for a non-empty problem,
+                                                  negative size, size overflow,
+                                                  pointer not aligned to its element,
+                                                  prefetch_stages < -1, bad option */
+    GEMM_MKL_STATUS_UNSUPPORTED_DTYPE = -2,    /* dtype not one of GEMM_MKL_F32/F16/BF16 */
+    GEMM_MKL_STATUS_UNSUPPORTED_EPILOGUE = -3, /* epilogue not one of GEMM_MKL_EPI_* */
+    GEMM_MKL_STATUS_WORKSPACE = -4,            /* caller workspace too small, or the
+                                                  internal one could not be allocated */
+    GEMM_MKL_STATUS_HIP_ERROR = -5,            /* a HIP runtime call failed */
+    GEMM_MKL_STATUS_NOT_AVAILABLE = -6         /* the forced kernel configuration /
+                                                  prefetch depth does not exist or does
+                                                  not fit this problem */
+};
+
+/*
+ * The GEMM.  Sizes are element counts (M, N, K, L >= 0).
+ *   M*N*L == 0  -> success, nothing launched.
+ *   K == 0      -> C = epilogue(0) = 0.
+ * The library picks the kernel configuration (tile, prefetch depth, split-K
+ * factor) from the problem shape.  When it splits K, it sums the fp32 partial
+ * results in a fixed order in a workspace it owns (see gemm_mkl_release_workspace);
+ * results are bitwise reproducible from run to run.
+ */
+int gemm_mkl(const void *A, const void *B, void *C,
+             int64_t M, int64_t N, int64_t K, int64_t L,
+             int dtype, int epilogue, void *stream);
+
+/*
+ * Options for gemm_mkl_ex.  Initialise with gemm_mkl_opts_init (all automatic),
+ * then set what you need.
+ *
+ * prefetch_stages: number of K chunks loaded ahead of the one being consumed
+ *   (the global -> LDS prefetch ring holds prefetch_stages + 1 chunks); 0 is
+ *   load-then-use with no prefetch, -1 is automatic.  Below -1 is
+ *   INVALID_VALUE (the depth must be 0 or greater); a depth that no kernel
+ *   configuration provides is NOT_AVAILABLE.
+ * split_k: number of K ranges computed by separate workgroups and summed in
+ *   ascending order of range (0 = auto, 1 = no split, at most 16).  Ranges
+ *   that would be empty are dropped.
+ * config_id: index into the kernel configuration table (-1 = auto); see
+ *   gemm_mkl_config_name.  A configuration of another dtype is NOT_AVAILABLE.
+ * flags: GEMM_MKL_OPT_FORCE_GENERAL selects the general kernel.
+ * workspace / workspace_bytes: caller-owned device memory for the split-K
+ *   partial sums (NULL = use the library's internal workspace).  It must hold
+ *   the plan's workspace_bytes (gemm_mkl_get_plan) and be 256-byte aligned;
+ *   too small is GEMM_MKL_STATUS_WORKSPACE.
+ *
+ * The environment variables GEMM_MKL_FORCE_CONFIG, GEMM_MKL_STAGES and
+ * GEMM_MKL_SPLIT_K supply the same three choices when opts leaves them
+ * automatic (for sweeps); GEMM_MKL_LOG=1 prints each call's plan to stderr;
+ * GEMM_MKL_WORKSPACE_LIMIT=<bytes> caps the internal workspace.
+ */
+typedef struct gemm_mkl_opts {
+    int32_t prefetch_stages; /* -1 = auto */
+    int32_t split_k;         /* 0 = auto */
+    int32_t config_id;       /* -1 = auto */
+    int32_t flags;           /* GEMM_MKL_OPT_* bits */
+    void *workspace;         /* device pointer or NULL */
+    size_t workspace_bytes;
+} gemm_mkl_opts;
+
+/* flags */
+enum {
+    GEMM_MKL_OPT_FORCE_GENERAL = 1 /* use the general (unaligned-capable) kernel */
+};
+
+/* Initialise opts to "all automatic". */
+void gemm_mkl_opts_init(gemm_mkl_opts *opts);
+
+/* The GEMM with explicit options (opts == NULL is the same as gemm_mkl). */
+int gemm_mkl_ex(const void *A, const void *B, void *C,
+                int64_t M, int64_t N, int64_t K, int64_t L,
+                int dtype, int epilogue, void *stream,
+                const gemm_mkl_opts *opts);
+
+/*
+ * The plan gemm_mkl_ex would execute for these arguments, without launching
+ * anything: chosen configuration id, prefetch depth, split factor, grid size
+ * and workspace bytes.  Returns a status like gemm_mkl_ex (argument checks
+ * are the same; pointers are not needed).
+ */
+typedef struct gemm_mkl_plan {
+    int32_t config_id;
+    int32_t prefetch_stages;
+    int32_t split_k;
+    int32_t general;          /* 1 if the general kernel is used */
+    int64_t grid;             /* workgroups of the main kernel */
+    int32_t block_m, block_n, block_k, threads;
+    size_t workspace_bytes;   /* 0 when split_k == 1 */
+} gemm_mkl_plan;
+
+int gemm_mkl_get_plan(int64_t M, int64_t N, int64_t K, int64_t L,
+                      int dtype, int epilogue, const gemm_mkl_opts *opts,
+                      gemm_mkl_plan *plan);
+
+/* Bytes of split-K workspace for the plan of these arguments (0 if none). */
+size_t gemm_mkl_workspace_size(int64_t M, int64_t N, int64_t K, int64_t L,
+                               int dtype, int split_k);
+
+/* Frees the internal split-K workspaces of every device (call with no GEMM in
+ * flight).  Returns GEMM_MKL_STATUS_OK or GEMM_MKL_STATUS_HIP_ERROR. */
+int gemm_mkl_release_workspace(void);
+
+/* A static, human-readable description of a status code (never NULL).  For
+ * GEMM_MKL_STATUS_HIP_ERROR it names the last HIP error seen by this thread. */
+const char *gemm_mkl_status_string(int status);
+
+/* Number of entries in the kernel configuration table, and a static
+ * description of entry `id` (NULL if out of range). */
+int gemm_mkl_num_configs(void);
+const char *gemm_mkl_config_name(int id);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int gemm_mkl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_MKL_H_ */

@@ -19,5 +19,6 @@ from .oracle import (  # noqa: F401
     gemm_rounded,
     load,
     round_to_dtype,
+    threads,
     widen,
 )

@@ -236,3 +236,13 @@ int oracle_gemm_entries(const void *A, const void *B,
     }
     return used;
 }
+
+/* Number of OpenMP threads the oracle's parallel loops use (1 without OpenMP). */
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -68,6 +68,8 @@ def _bind(lib):
     lib.oracle_widen.restype = None
     lib.oracle_epilogue.argtypes = [ctypes.c_double, ctypes.c_int]
     lib.oracle_epilogue.restype = ctypes.c_double
+    lib.oracle_threads.argtypes = []
+    lib.oracle_threads.restype = ctypes.c_int
     return lib
 
 
@@ -137,6 +139,11 @@ def widen(x: np.ndarray, dtype: str, lib=None) -> np.ndarray:
     out = np.empty(x.shape, dtype=np.float64)
     (lib or load()).oracle_widen(_ptr(x), _ptr(out), x.size, DTYPES[dtype])
     return out
+
+
+def threads(lib=None) -> int:
+    """OpenMP threads the oracle uses on this host."""
+    return int((lib or load()).oracle_threads())
 
 
 def epilogue64(x: float, epilogue: str, lib=None) -> float:

@@ -1,0 +1,184 @@
+"""CPU tests of the C ABI: exported symbols, argument checks, plans.
+
+No call here reaches a kernel launch: every call is either rejected by the
+argument checks (which run before any HIP call) or describes an empty problem.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tiled_dense_gemm_mkl_amd as gm
+from tiled_dense_gemm_mkl_amd import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm_mkl.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gm.LIB_PATH):
+        pytest.skip("libgemm_mkl.so is not built (run python -m tiled_dense_gemm_mkl_amd.build)")
+    return gm.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(gemm_mkl\w*)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_what_the_binding_expects():
+    assert declared_functions() == sorted(gm.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} is declared in gemm_mkl.h but not exported"
+
+
+def test_version(lib):
+    assert lib.gemm_mkl_version() >= 100
+
+
+BF16, F32, F16 = gm.BF16, gm.F32, gm.F16
+ID, RELU, SILU = gm.EPI_IDENTITY, gm.EPI_RELU, gm.EPI_SILU
+FAKE = 0x10000  # never dereferenced: every call below is rejected before any launch
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, FAKE, FAKE, 4, 4, 4, 1, 7, ID), -2),            # unknown dtype
+    ((FAKE, FAKE, FAKE, 4, 4, 4, 1, -1, ID), -2),
+    ((FAKE, FAKE, FAKE, 4, 4, 4, 1, BF16, 3), -3),          # unknown epilogue
+    ((FAKE, FAKE, FAKE, -1, 4, 4, 1, BF16, ID), -1),        # negative sizes
+    ((FAKE, FAKE, FAKE, 4, -4, 4, 1, BF16, ID), -1),
+    ((FAKE, FAKE, FAKE, 4, 4, -4, 1, BF16, ID), -1),
+    ((FAKE, FAKE, FAKE, 4, 4, 4, -1, BF16, ID), -1),
+    ((FAKE, FAKE, None, 4, 4, 4, 1, BF16, ID), -1),         # null C
+    ((None, FAKE, FAKE, 4, 4, 4, 1, BF16, ID), -1),         # null A with K > 0
+    ((FAKE, None, FAKE, 4, 4, 4, 1, F32, RELU), -1),        # null B with K > 0
+    ((FAKE + 1, FAKE, FAKE, 4, 4, 4, 1, BF16, ID), -1),     # A not aligned to its element
+    ((FAKE, FAKE, FAKE + 2, 4, 4, 4, 1, F32, ID), -1),      # C not aligned to fp32
+    ((FAKE, FAKE, FAKE, 2 ** 40, 2 ** 40, 2 ** 40, 1, BF16, ID), -1),  # byte sizes overflow
+    ((None, None, None, 0, 4, 4, 1, BF16, ID), 0),          # empty problems: no launch
+    ((None, None, None, 4, 0, 4, 1, F32, SILU), 0),
+    ((None, None, None, 4, 4, 4, 0, F16, RELU), 0),
+    ((None, None, None, 0, 0, 0, 0, BF16, ID), 0),
+])
+def test_argument_checks(lib, args, status):
+    assert gm.gemm_mkl(*args, None) == status
+
+
+def test_dtype_checked_before_epilogue(lib):
+    assert gm.gemm_mkl(FAKE, FAKE, FAKE, 4, 4, 4, 1, 9, 9, None) == -2
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(prefetch_stages=-2), -1),       # a negative prefetch depth is invalid
+    (dict(prefetch_stages=-7), -1),
+    (dict(split_k=-1), -1),
+    (dict(config_id=-5), -1),
+    (dict(config_id=10_000), -6),         # no such configuration
+    (dict(prefetch_stages=9), -6),        # no kernel with that ring depth
+    (dict(split_k=17), -6),
+])
+def test_option_checks(lib, kw, status):
+    o = gm.make_opts(**kw)
+    assert gm.gemm_mkl_ex(FAKE, FAKE, None, 4, 4, 4, 1, BF16, ID, None, o) in (status, -1)
+    # the plan query applies the same checks without pointers
+    try:
+        gm.get_plan(64, 64, 64, 1, BF16, ID, o)
+        got = 0
+    except gm.GemmMklError as e:
+        got = e.status
+    assert got == status
+
+
+def test_config_of_another_dtype_is_not_available(lib):
+    names = gm.config_names()
+    f32_ids = [i for i, n in enumerate(names) if n.startswith("f32")]
+    assert f32_ids
+    with pytest.raises(gm.GemmMklError) as e:
+        gm.get_plan(256, 256, 256, 1, BF16, ID, gm.make_opts(config_id=f32_ids[0]))
+    assert e.value.status == -6
+
+
+def test_workspace_flags_and_alignment(lib):
+    o = gm.make_opts(workspace_ptr=FAKE + 16, workspace_bytes=1 << 20)  # not 256-byte aligned
+    with pytest.raises(gm.GemmMklError):
+        gm.get_plan(64, 64, 64, 1, BF16, ID, o)
+    o = gm.make_opts()
+    o.flags = 0x40  # unknown flag bit
+    with pytest.raises(gm.GemmMklError):
+        gm.get_plan(64, 64, 64, 1, BF16, ID, o)
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5, -6, 123):
+        s = gm.status_string(code)
+        assert isinstance(s, str) and s
+    assert "prefetch_stages" in gm.status_string(-1)
+    assert gm.status_string(0) == "success"
+    assert gm.status_string(123) == "unknown status"
+
+
+def test_config_table(lib):
+    names = gm.config_names()
+    assert len(names) == lib.gemm_mkl_num_configs() >= 3
+    for prefix in ("f32", "f16", "bf16"):
+        assert any(n.startswith(prefix + " ") for n in names)
+    assert lib.gemm_mkl_config_name(-1) is None
+    assert lib.gemm_mkl_config_name(len(names)) is None
+
+
+@pytest.mark.parametrize("key", list(workloads.WORKLOADS))
+def test_plans_of_the_workloads(lib, key):
+    w = workloads.WORKLOADS[key]
+    code = gm.DTYPE_CODES[w.dtype]
+    epi = gm.EPILOGUE_CODES[w.epilogue]
+    p = gm.get_plan(w.M, w.N, w.K, w.L, code, epi)
+    assert p["general"] == 0
+    tiles = -(-w.M // p["block_m"]) * -(-w.N // p["block_n"]) * w.L
+    assert p["grid"] == tiles * p["split_k"]
+    assert p["block_k"] * (4 if w.dtype == "f32" else 2) == 128
+    if p["split_k"] > 1:
+        assert p["workspace_bytes"] == p["split_k"] * w.L * w.M * w.N * 4
+    else:
+        assert p["workspace_bytes"] == 0
+    # a forced split of the K-heavy shape goes through the split-K path
+    p2 = gm.get_plan(w.M, w.N, w.K, w.L, code, epi, gm.make_opts(split_k=2))
+    assert p2["split_k"] == 2 and p2["workspace_bytes"] == 2 * w.L * w.M * w.N * 4
+    assert gm.workspace_size(w.M, w.N, w.K, w.L, code, 2) == p2["workspace_bytes"]
+
+
+def test_unaligned_K_takes_the_general_kernel(lib):
+    p = gm.get_plan(33, 17, 13, 2, BF16, RELU)     # K * 2 bytes is not a multiple of 16
+    assert p["general"] == 1 and p["split_k"] == 1
+    p = gm.get_plan(33, 17, 16, 2, BF16, RELU)
+    assert p["general"] == 0
+    with pytest.raises(gm.GemmMklError) as e:      # a split cannot be forced on it
+        gm.get_plan(33, 17, 13, 2, BF16, RELU, gm.make_opts(split_k=2))
+    assert e.value.status == -6
+
+
+def test_every_prefetch_depth_of_a_config_is_plannable(lib):
+    names = gm.config_names()
+    for cid, name in enumerate(names):
+        dt = gm.DTYPE_CODES[name.split()[0]]
+        ok = []
+        for p in range(0, 5):
+            try:
+                plan = gm.get_plan(300, 300, 1000, 1, dt, ID, gm.make_opts(config_id=cid, prefetch_stages=p))
+                assert plan["prefetch_stages"] == p and plan["config_id"] == cid
+                ok.append(p)
+            except gm.GemmMklError as e:
+                assert e.status == -6
+        assert ok, f"config {name} has no prefetch depth"
+
+
+def test_ctypes_struct_sizes_match_header(lib):
+    # gemm_mkl_opts: 4 x int32, pointer, size_t ; gemm_mkl_plan: 4 x int32, int64, 4 x int32, size_t
+    assert ctypes.sizeof(gm._binding.Opts) == 32
+    assert ctypes.sizeof(gm._binding.Plan) == 48

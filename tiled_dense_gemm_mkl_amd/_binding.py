@@ -1,0 +1,238 @@
+"""ctypes binding of libgemm_mkl.so: argument marshalling only.
+
+Every step of the GEMM runs in the HIP library.  There is no fallback: if the
+library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libgemm_mkl.so")
+
+F32, F16, BF16 = 0, 1, 2
+EPI_IDENTITY, EPI_RELU, EPI_SILU = 0, 1, 2
+STATUS = {
+    0: "OK",
+    -1: "INVALID_VALUE",
+    -2: "UNSUPPORTED_DTYPE",
+    -3: "UNSUPPORTED_EPILOGUE",
+    -4: "WORKSPACE",
+    -5: "HIP_ERROR",
+    -6: "NOT_AVAILABLE",
+}
+OPT_FORCE_GENERAL = 1
+
+DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16}
+EPILOGUE_CODES = {"identity": EPI_IDENTITY, "relu": EPI_RELU, "silu": EPI_SILU}
+
+
+class GemmMklError(RuntimeError):
+    """A non-zero status from the C ABI."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"gemm_mkl status {status} ({STATUS.get(status, '?')}): {message}")
+        self.status = status
+
+
+class Opts(ctypes.Structure):
+    _fields_ = [
+        ("prefetch_stages", ctypes.c_int32),
+        ("split_k", ctypes.c_int32),
+        ("config_id", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [
+        ("config_id", ctypes.c_int32),
+        ("prefetch_stages", ctypes.c_int32),
+        ("split_k", ctypes.c_int32),
+        ("general", ctypes.c_int32),
+        ("grid", ctypes.c_int64),
+        ("block_m", ctypes.c_int32),
+        ("block_n", ctypes.c_int32),
+        ("block_k", ctypes.c_int32),
+        ("threads", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+    def as_dict(self) -> dict:
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+EXPORTS = (
+    "gemm_mkl",
+    "gemm_mkl_ex",
+    "gemm_mkl_opts_init",
+    "gemm_mkl_get_plan",
+    "gemm_mkl_workspace_size",
+    "gemm_mkl_release_workspace",
+    "gemm_mkl_status_string",
+    "gemm_mkl_num_configs",
+    "gemm_mkl_config_name",
+    "gemm_mkl_version",
+)
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load and type the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build the HIP library first "
+            "(python -m tiled_dense_gemm_mkl_amd.build); there is no fallback path")
+    lib = ctypes.CDLL(path)
+    i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    lib.gemm_mkl.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i32, vp]
+    lib.gemm_mkl.restype = i32
+    lib.gemm_mkl_ex.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i32, vp, ctypes.POINTER(Opts)]
+    lib.gemm_mkl_ex.restype = i32
+    lib.gemm_mkl_opts_init.argtypes = [ctypes.POINTER(Opts)]
+    lib.gemm_mkl_opts_init.restype = None
+    lib.gemm_mkl_get_plan.argtypes = [i64, i64, i64, i64, i32, i32, ctypes.POINTER(Opts), ctypes.POINTER(Plan)]
+    lib.gemm_mkl_get_plan.restype = i32
+    lib.gemm_mkl_workspace_size.argtypes = [i64, i64, i64, i64, i32, i32]
+    lib.gemm_mkl_workspace_size.restype = ctypes.c_size_t
+    lib.gemm_mkl_release_workspace.argtypes = []
+    lib.gemm_mkl_release_workspace.restype = i32
+    lib.gemm_mkl_status_string.argtypes = [i32]
+    lib.gemm_mkl_status_string.restype = ctypes.c_char_p
+    lib.gemm_mkl_num_configs.argtypes = []
+    lib.gemm_mkl_num_configs.restype = i32
+    lib.gemm_mkl_config_name.argtypes = [i32]
+    lib.gemm_mkl_config_name.restype = ctypes.c_char_p
+    lib.gemm_mkl_version.argtypes = []
+    lib.gemm_mkl_version.restype = i32
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().gemm_mkl_status_string(int(status)).decode()
+
+
+def make_opts(prefetch_stages=None, split_k=None, config_id=None, force_general=False,
+              workspace_ptr=None, workspace_bytes=0) -> Opts:
+    o = Opts()
+    load().gemm_mkl_opts_init(ctypes.byref(o))
+    if prefetch_stages is not None:
+        o.prefetch_stages = int(prefetch_stages)
+    if split_k is not None:
+        o.split_k = int(split_k)
+    if config_id is not None:
+        o.config_id = int(config_id)
+    if force_general:
+        o.flags |= OPT_FORCE_GENERAL
+    if workspace_ptr is not None:
+        o.workspace = int(workspace_ptr)
+        o.workspace_bytes = int(workspace_bytes)
+    return o
+
+
+# ------------------------------------------------------------------ raw C-ABI calls
+
+def gemm_mkl(A_ptr, B_ptr, C_ptr, M, N, K, L, dtype, epilogue, stream=None) -> int:
+    """The C entry point, unchanged: device pointers as ints, returns the status."""
+    return load().gemm_mkl(A_ptr, B_ptr, C_ptr, M, N, K, L, dtype, epilogue, stream)
+
+
+def gemm_mkl_ex(A_ptr, B_ptr, C_ptr, M, N, K, L, dtype, epilogue, stream=None, opts: Opts | None = None) -> int:
+    return load().gemm_mkl_ex(A_ptr, B_ptr, C_ptr, M, N, K, L, dtype, epilogue, stream,
+                              ctypes.byref(opts) if opts is not None else None)
+
+
+def get_plan(M, N, K, L, dtype, epilogue, opts: Opts | None = None) -> dict:
+    p = Plan()
+    st = load().gemm_mkl_get_plan(M, N, K, L, dtype, epilogue,
+                                  ctypes.byref(opts) if opts is not None else None, ctypes.byref(p))
+    if st != 0:
+        raise GemmMklError(st, status_string(st))
+    return p.as_dict()
+
+
+def workspace_size(M, N, K, L, dtype, split_k=0) -> int:
+    return int(load().gemm_mkl_workspace_size(M, N, K, L, dtype, split_k))
+
+
+def release_workspace() -> None:
+    st = load().gemm_mkl_release_workspace()
+    if st != 0:
+        raise GemmMklError(st, status_string(st))
+
+
+def config_names() -> list[str]:
+    lib = load()
+    return [lib.gemm_mkl_config_name(i).decode() for i in range(lib.gemm_mkl_num_configs())]
+
+
+# ------------------------------------------------------------------ torch front end
+
+def _torch_dtype_code(t) -> int:
+    import torch
+
+    codes = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}: expected float32, float16 or bfloat16")
+    return codes[t.dtype]
+
+
+def gemm(a, b, epilogue: str = "identity", out=None, *, prefetch_stages=None, split_k=None,
+         config_id=None, force_general=False, workspace=None, stream=None):
+    """C = epilogue(a @ b^T) per batch, on the GPU through libgemm_mkl.
+
+    a: [L, M, K] or [M, K]; b: [L, N, K] or [N, K] (same dtype, on one GPU,
+    contiguous).  Returns [L, M, N] (or [M, N]) in the operand dtype.
+    """
+    import torch
+
+    if epilogue not in EPILOGUE_CODES:
+        raise ValueError(f"unknown epilogue {epilogue!r}: expected one of {sorted(EPILOGUE_CODES)}")
+    if not (isinstance(a, torch.Tensor) and isinstance(b, torch.Tensor)):
+        raise TypeError("a and b must be torch tensors")
+    if a.device.type != "cuda" or b.device != a.device:
+        raise ValueError("a and b must be on the same GPU")
+    if a.dtype != b.dtype:
+        raise TypeError(f"dtype mismatch: a is {a.dtype}, b is {b.dtype}")
+    squeeze = a.dim() == 2
+    if squeeze:
+        if b.dim() != 2:
+            raise ValueError("a and b must both be 2-D or both 3-D")
+        a3, b3 = a.unsqueeze(0), b.unsqueeze(0)
+    else:
+        if a.dim() != 3 or b.dim() != 3:
+            raise ValueError("a must be [L, M, K] and b [L, N, K]")
+        a3, b3 = a, b
+    L, M, K = a3.shape
+    Lb, N, Kb = b3.shape
+    if Lb != L or Kb != K:
+        raise ValueError(f"shape mismatch: a {tuple(a.shape)}, b {tuple(b.shape)}")
+    if not (a3.is_contiguous() and b3.is_contiguous()):
+        raise ValueError("a and b must be contiguous (K innermost)")
+    if out is None:
+        out3 = torch.empty((L, M, N), dtype=a.dtype, device=a.device)
+    else:
+        out3 = out.unsqueeze(0) if squeeze else out
+        if tuple(out3.shape) != (L, M, N) or out3.dtype != a.dtype or not out3.is_contiguous() \
+                or out3.device != a.device:
+            raise ValueError("out must be a contiguous [L, M, N] tensor of the operand dtype on the same GPU")
+    ws_ptr = ws_bytes = None
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    opts = make_opts(prefetch_stages, split_k, config_id, force_general, ws_ptr, ws_bytes or 0)
+    s = stream if stream is not None else torch.cuda.current_stream(a.device)
+    with torch.cuda.device(a.device):
+        st = gemm_mkl_ex(a3.data_ptr(), b3.data_ptr(), out3.data_ptr(), M, N, K, L,
+                         _torch_dtype_code(a), EPILOGUE_CODES[epilogue], s.cuda_stream, opts)
+    if st != 0:
+        raise GemmMklError(st, status_string(st))
+    return out3[0] if squeeze else out3

@@ -1,0 +1,109 @@
+// configs.hpp -- the kernel configuration table shared by the host dispatcher
+// and the per-dtype instantiation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "gemm_kernels.hpp"
+
+namespace gmk {
+
+constexpr int kMaxPrefetch = 4;   // prefetch_stages 0..4 (ring of 1..5 LDS slots)
+constexpr int kModes = 4;         // identity, relu, silu, split-K partial
+
+typedef hipError_t (*TileLaunchFn)(const TileParams &p, int grid, hipStream_t stream);
+typedef hipError_t (*ReduceLaunchFn)(const float *W, void *C, int64_t total, int split, hipStream_t stream);
+typedef hipError_t (*GeneralLaunchFn)(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
+                                      int64_t L, hipStream_t stream);
+
+struct ConfigEntry {
+    int dtype;             // GEMM_MKL_F32 / F16 / BF16
+    int bm, bn;            // output tile
+    int waves_m, waves_n;  // wave grid (64 lanes each)
+    int default_p;         // prefetch_stages used when not forced
+    const char *name;
+    TileLaunchFn fn[kMaxPrefetch + 1][kModes];  // null where not instantiated
+};
+
+struct DtypeKernels {
+    ReduceLaunchFn reduce[3];    // by epilogue
+    GeneralLaunchFn general[3];  // by epilogue
+};
+
+// Filled by the instantiation units (one per dtype).
+void register_f32(std::vector<ConfigEntry> &table, DtypeKernels &k);
+void register_f16(std::vector<ConfigEntry> &table, DtypeKernels &k);
+void register_bf16(std::vector<ConfigEntry> &table, DtypeKernels &k);
+
+// ---------------------------------------------------------------- helpers for the units
+
+template <class T, int BM, int BN, int WMW, int WNW, int P, int MODE>
+hipError_t launch_tile(const TileParams &p, int grid, hipStream_t stream)
+{
+    hipLaunchKernelGGL((gemm_tile_kernel<T, BM, BN, WMW, WNW, P, MODE>), dim3(grid), dim3(WMW * WNW * 64), 0,
+                       stream, p);
+    return hipGetLastError();
+}
+
+template <class T, int BM, int BN, int WMW, int WNW, int P>
+void fill_prefetch(ConfigEntry &e)
+{
+    e.fn[P][MODE_IDENTITY] = &launch_tile<T, BM, BN, WMW, WNW, P, MODE_IDENTITY>;
+    e.fn[P][MODE_RELU] = &launch_tile<T, BM, BN, WMW, WNW, P, MODE_RELU>;
+    e.fn[P][MODE_SILU] = &launch_tile<T, BM, BN, WMW, WNW, P, MODE_SILU>;
+    e.fn[P][MODE_PARTIAL] = &launch_tile<T, BM, BN, WMW, WNW, P, MODE_PARTIAL>;
+}
+
+template <class T, int BM, int BN, int WMW, int WNW, int... Ps>
+ConfigEntry make_entry(int dtype, int default_p, const char *name)
+{
+    ConfigEntry e{};
+    e.dtype = dtype;
+    e.bm = BM;
+    e.bn = BN;
+    e.waves_m = WMW;
+    e.waves_n = WNW;
+    e.default_p = default_p;
+    e.name = name;
+    (fill_prefetch<T, BM, BN, WMW, WNW, Ps>(e), ...);
+    return e;
+}
+
+template <class T, int MODE>
+hipError_t launch_reduce(const float *W, void *C, int64_t total, int split, hipStream_t stream)
+{
+    int64_t per_thread = (total % 4 == 0) ? 4 : 1;
+    int64_t blocks = (total / per_thread + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL((splitk_reduce_kernel<T, MODE>), dim3((unsigned)blocks), dim3(256), 0, stream, W,
+                       reinterpret_cast<T *>(C), total, split);
+    return hipGetLastError();
+}
+
+template <class T, int MODE>
+hipError_t launch_general(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int64_t L,
+                          hipStream_t stream)
+{
+    const int64_t tm = (M + 63) / 64, tn = (N + 63) / 64;
+    hipLaunchKernelGGL((gemm_general_kernel<T, MODE>), dim3((unsigned)(tm * tn * L)), dim3(256), 0, stream,
+                       reinterpret_cast<const T *>(A), reinterpret_cast<const T *>(B), reinterpret_cast<T *>(C),
+                       M, N, K, (int32_t)tm, (int32_t)tn);
+    return hipGetLastError();
+}
+
+template <class T>
+void fill_dtype_kernels(DtypeKernels &k)
+{
+    k.reduce[0] = &launch_reduce<T, MODE_IDENTITY>;
+    k.reduce[1] = &launch_reduce<T, MODE_RELU>;
+    k.reduce[2] = &launch_reduce<T, MODE_SILU>;
+    k.general[0] = &launch_general<T, MODE_IDENTITY>;
+    k.general[1] = &launch_general<T, MODE_RELU>;
+    k.general[2] = &launch_general<T, MODE_SILU>;
+}
+
+}  // namespace gmk

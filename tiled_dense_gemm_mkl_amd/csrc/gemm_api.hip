@@ -1,0 +1,470 @@
+// gemm_api.hip -- the C ABI (include/gemm_mkl.h): argument checks, the
+// configuration choice, the split-K workspace and the kernel launches.
+//
+// The boundary takes plain device pointers, sizes, a dtype, an epilogue and a
+// stream, as the GEMM entry of "深入解析 CUTLASS CuTe DSL 的 JIT 函数参数生成机制"
+// (section 2.3) takes tensors, a stream and a compile-time epilogue.  Bad
+// arguments are rejected before any HIP call, with a code that names the
+// problem (the type-check errors of section 3.1 there); a negative prefetch
+// depth is rejected as the loop-attribute diagnostic of section 3 of
+// "CUTLASS CuTe DSL 控制流编程指南" does.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "../../include/gemm_mkl.h"
+#include "configs.hpp"
+
+using namespace gmk;
+
+namespace {
+
+constexpr int kNumCUs = 256;          // MI355X compute units (8 XCDs x 32)
+constexpr int64_t kMaxSplit = 16;
+
+struct Registry {
+    std::vector<ConfigEntry> table;
+    DtypeKernels k[3];
+    Registry()
+    {
+        register_f32(table, k[GEMM_MKL_F32]);
+        register_f16(table, k[GEMM_MKL_F16]);
+        register_bf16(table, k[GEMM_MKL_BF16]);
+    }
+};
+
+Registry &registry()
+{
+    static Registry r;
+    return r;
+}
+
+thread_local hipError_t t_last_hip = hipSuccess;
+thread_local char t_hip_msg[192];
+
+int elem_bytes(int dtype) { return dtype == GEMM_MKL_F32 ? 4 : 2; }
+
+int env_int(const char *name, int dflt)
+{
+    const char *v = std::getenv(name);
+    if (!v || !*v) return dflt;
+    return std::atoi(v);
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t *out)
+{
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+struct Plan {
+    int config_id = -1;
+    int P = 0;
+    int S = 1;
+    bool general = false;
+    int64_t grid = 0;
+    int32_t tiles_m = 0, tiles_n = 0;
+    int32_t total_chunks = 0, chunks_per_split = 0;
+    size_t ws_bytes = 0;
+};
+
+int check_args(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, int epilogue, const gemm_mkl_opts *o)
+{
+    if (dtype != GEMM_MKL_F32 && dtype != GEMM_MKL_F16 && dtype != GEMM_MKL_BF16)
+        return GEMM_MKL_STATUS_UNSUPPORTED_DTYPE;
+    if (epilogue != GEMM_MKL_EPI_IDENTITY && epilogue != GEMM_MKL_EPI_RELU && epilogue != GEMM_MKL_EPI_SILU)
+        return GEMM_MKL_STATUS_UNSUPPORTED_EPILOGUE;
+    if (M < 0 || N < 0 || K < 0 || L < 0) return GEMM_MKL_STATUS_INVALID_VALUE;
+    // every operand's byte size must fit in int64
+    const int64_t es = elem_bytes(dtype);
+    int64_t t;
+    if (!mul_ok(M, K, &t) || !mul_ok(t, L, &t) || !mul_ok(t, es, &t)) return GEMM_MKL_STATUS_INVALID_VALUE;
+    if (!mul_ok(N, K, &t) || !mul_ok(t, L, &t) || !mul_ok(t, es, &t)) return GEMM_MKL_STATUS_INVALID_VALUE;
+    if (!mul_ok(M, N, &t) || !mul_ok(t, L, &t) || !mul_ok(t, 4 * kMaxSplit, &t))
+        return GEMM_MKL_STATUS_INVALID_VALUE;
+    if (o) {
+        if (o->prefetch_stages < -1) return GEMM_MKL_STATUS_INVALID_VALUE;
+        if (o->split_k < 0) return GEMM_MKL_STATUS_INVALID_VALUE;
+        if (o->config_id < -1) return GEMM_MKL_STATUS_INVALID_VALUE;
+        if (o->flags & ~(int32_t)GEMM_MKL_OPT_FORCE_GENERAL) return GEMM_MKL_STATUS_INVALID_VALUE;
+        if (o->workspace == nullptr && o->workspace_bytes != 0) return GEMM_MKL_STATUS_INVALID_VALUE;
+        if (o->workspace && (reinterpret_cast<uintptr_t>(o->workspace) & 255)) return GEMM_MKL_STATUS_INVALID_VALUE;
+    }
+    return GEMM_MKL_STATUS_OK;
+}
+
+// Modelled time of one configuration, in cycles of one CU, for the heuristic.
+double model_cycles(const ConfigEntry &c, int dtype, int64_t M, int64_t N, int64_t K, int64_t L, int S,
+                    int total_chunks)
+{
+    const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn) * L;
+    const int64_t units = tiles * S;
+    const int64_t rounds = (units + kNumCUs - 1) / kNumCUs;
+    const int chunks = (total_chunks + S - 1) / S;
+    const double bk = 128.0 / elem_bytes(dtype);
+    const double peak = dtype == GEMM_MKL_F32 ? 256.0 : 4096.0;  // flop / clk / CU
+    double eff;
+    const int area = c.bm * c.bn;
+    if (dtype == GEMM_MKL_F32)
+        eff = area >= 128 * 128 ? 0.8 : (area >= 64 * 64 ? 0.7 : 0.5);
+    else
+        eff = area >= 256 * 128 ? 0.75 : (area >= 128 * 128 ? 0.65 : 0.3);
+    const double per_chunk = 2.0 * c.bm * c.bn * bk / (peak * eff) + 60.0;
+    double cyc = (double)rounds * (chunks * per_chunk + 1500.0);
+    if (S > 1) {
+        const double out = (double)L * M * N;
+        const double bytes = out * 4.0 * S * 2.0 + out * elem_bytes(dtype);
+        cyc += bytes / 2000.0 + 5000.0;  // ~4.8 TB/s and one more launch
+    }
+    return cyc;
+}
+
+bool fast_path_ok(const ConfigEntry &c, int dtype, int64_t K)
+{
+    const int64_t es = elem_bytes(dtype);
+    if ((K * es) % 16 != 0) return false;
+    // offsets inside one tile's buffer resource must stay below 2^31
+    if (((int64_t)c.bm + 1) * K * es + 256 >= (int64_t)kOutOfRange) return false;
+    if (((int64_t)c.bn + 1) * K * es + 256 >= (int64_t)kOutOfRange) return false;
+    return true;
+}
+
+int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_mkl_opts *o, bool ptrs_aligned,
+              Plan *plan)
+{
+    Registry &R = registry();
+    const int64_t es = elem_bytes(dtype);
+    int forced_cfg = o ? o->config_id : -1;
+    if (forced_cfg < 0) forced_cfg = env_int("GEMM_MKL_FORCE_CONFIG", -1);
+    int forced_p = o ? o->prefetch_stages : -1;
+    if (forced_p < 0) forced_p = env_int("GEMM_MKL_STAGES", -1);
+    int forced_s = o ? o->split_k : 0;
+    if (forced_s <= 0) forced_s = env_int("GEMM_MKL_SPLIT_K", 0);
+    const bool force_general = o && (o->flags & GEMM_MKL_OPT_FORCE_GENERAL);
+
+    if (forced_cfg >= (int)R.table.size()) return GEMM_MKL_STATUS_NOT_AVAILABLE;
+    if (forced_cfg >= 0 && R.table[forced_cfg].dtype != dtype) return GEMM_MKL_STATUS_NOT_AVAILABLE;
+    if (forced_p > kMaxPrefetch) return GEMM_MKL_STATUS_NOT_AVAILABLE;
+    if (forced_s > kMaxSplit) return GEMM_MKL_STATUS_NOT_AVAILABLE;
+
+    const int64_t total_chunks64 = (K * es + 127) / 128;
+    if (total_chunks64 > INT32_MAX) return GEMM_MKL_STATUS_NOT_AVAILABLE;
+    const int total_chunks = (int)total_chunks64;
+
+    bool general = force_general || !ptrs_aligned;
+    if (!general) {
+        if (forced_cfg >= 0) {
+            if (!fast_path_ok(R.table[forced_cfg], dtype, K)) general = true;
+        } else {
+            bool any = false;
+            for (const ConfigEntry &c : R.table)
+                if (c.dtype == dtype && fast_path_ok(c, dtype, K)) any = true;
+            general = !any;
+        }
+    }
+    if (general) {
+        if (forced_cfg >= 0 || forced_p >= 0 || forced_s > 1) return GEMM_MKL_STATUS_NOT_AVAILABLE;
+        plan->general = true;
+        plan->config_id = -1;
+        plan->P = 0;
+        plan->S = 1;
+        plan->tiles_m = (int32_t)((M + 63) / 64);
+        plan->tiles_n = (int32_t)((N + 63) / 64);
+        plan->grid = (int64_t)plan->tiles_m * plan->tiles_n * L;
+        if (plan->grid > INT32_MAX) return GEMM_MKL_STATUS_NOT_AVAILABLE;
+        plan->ws_bytes = 0;
+        return GEMM_MKL_STATUS_OK;
+    }
+
+    // candidate (config, split) pairs
+    double best = 1e300;
+    int best_c = -1, best_s = 1;
+    for (int id = 0; id < (int)R.table.size(); ++id) {
+        const ConfigEntry &c = R.table[id];
+        if (c.dtype != dtype) continue;
+        if (forced_cfg >= 0 && id != forced_cfg) continue;
+        if (!fast_path_ok(c, dtype, K)) continue;
+        const int p = forced_p >= 0 ? forced_p : c.default_p;
+        if (c.fn[p][0] == nullptr) continue;
+        for (int S = 1; S <= kMaxSplit; ++S) {
+            if (forced_s > 0 && S != forced_s) continue;
+            if (forced_s <= 0 && S > 1 && (total_chunks + S - 1) / S < 4) break;
+            if (forced_s <= 0 && S != 1 && S != 2 && S != 3 && S != 4 && S != 6 && S != 8 && S != 12 && S != 16)
+                continue;
+            const double cyc = model_cycles(c, dtype, M, N, K, L, S, total_chunks);
+            if (cyc < best) {
+                best = cyc;
+                best_c = id;
+                best_s = S;
+            }
+        }
+    }
+    if (best_c < 0) return GEMM_MKL_STATUS_NOT_AVAILABLE;
+    const ConfigEntry &c = R.table[best_c];
+    plan->general = false;
+    plan->config_id = best_c;
+    plan->P = forced_p >= 0 ? forced_p : c.default_p;
+    plan->S = best_s;
+    plan->tiles_m = (int32_t)((M + c.bm - 1) / c.bm);
+    plan->tiles_n = (int32_t)((N + c.bn - 1) / c.bn);
+    plan->total_chunks = total_chunks;
+    plan->chunks_per_split = (total_chunks + best_s - 1) / best_s;
+    if (plan->chunks_per_split == 0) plan->chunks_per_split = 1;
+    // splits whose chunk range would be empty are dropped (the grid shrinks)
+    if (best_s > 1) {
+        int used = (total_chunks + plan->chunks_per_split - 1) / plan->chunks_per_split;
+        if (used < 1) used = 1;
+        plan->S = used;
+    }
+    plan->grid = (int64_t)plan->tiles_m * plan->tiles_n * plan->S * L;
+    if (plan->grid > INT32_MAX) return GEMM_MKL_STATUS_NOT_AVAILABLE;
+    plan->ws_bytes = plan->S > 1 ? (size_t)plan->S * (size_t)(L * M * N) * 4 : 0;
+    return GEMM_MKL_STATUS_OK;
+}
+
+// ---------------------------------------------------------------- internal workspace
+
+struct Workspace {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+int get_workspace(hipStream_t stream, size_t need, void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        t_last_hip = e;
+        return GEMM_MKL_STATUS_HIP_ERROR;
+    }
+    const char *lim = std::getenv("GEMM_MKL_WORKSPACE_LIMIT");
+    if (lim && *lim && need > (size_t)std::strtoull(lim, nullptr, 10)) return GEMM_MKL_STATUS_WORKSPACE;
+    std::lock_guard<std::mutex> g(g_ws_mutex);
+    Workspace &w = g_ws[std::make_pair(dev, stream)];
+    if (w.bytes < need) {
+        if (w.ptr) {
+            // the old buffer may still be read by work queued on this stream
+            e = hipStreamSynchronize(stream);
+            if (e == hipSuccess) e = hipFree(w.ptr);
+            w.ptr = nullptr;
+            w.bytes = 0;
+            if (e != hipSuccess) {
+                t_last_hip = e;
+                return GEMM_MKL_STATUS_HIP_ERROR;
+            }
+        }
+        size_t sz = need < ((size_t)1 << 20) ? ((size_t)1 << 20) : need;
+        e = hipMalloc(&w.ptr, sz);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            w.ptr = nullptr;
+            return GEMM_MKL_STATUS_WORKSPACE;
+        }
+        w.bytes = sz;
+    }
+    *out = w.ptr;
+    return GEMM_MKL_STATUS_OK;
+}
+
+int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int64_t L, int dtype, int epilogue,
+        void *stream_v, const gemm_mkl_opts *o)
+{
+    int st = check_args(M, N, K, L, dtype, epilogue, o);
+    if (st != GEMM_MKL_STATUS_OK) return st;
+    if (M == 0 || N == 0 || L == 0) return GEMM_MKL_STATUS_OK;
+    if (C == nullptr) return GEMM_MKL_STATUS_INVALID_VALUE;
+    if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_MKL_STATUS_INVALID_VALUE;
+    const int es = elem_bytes(dtype);
+    auto al = [](const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; };
+    if (!al(A, es) || !al(B, es) || !al(C, es)) return GEMM_MKL_STATUS_INVALID_VALUE;
+    const bool aligned = al(A, 16) && al(B, 16) && al(C, 4 * es);
+
+    Plan plan;
+    st = make_plan(M, N, K, L, dtype, o, aligned, &plan);
+    if (st != GEMM_MKL_STATUS_OK) return st;
+
+    Registry &R = registry();
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+    if (env_int("GEMM_MKL_LOG", 0))
+        std::fprintf(stderr, "gemm_mkl: M=%lld N=%lld K=%lld L=%lld dtype=%d epi=%d -> %s P=%d S=%d grid=%lld\n",
+                     (long long)M, (long long)N, (long long)K, (long long)L, dtype, epilogue,
+                     plan.general ? "general" : R.table[plan.config_id].name, plan.P, plan.S,
+                     (long long)plan.grid);
+
+    hipError_t e;
+    if (plan.general) {
+        e = R.k[dtype].general[epilogue](A, B, C, M, N, K, L, stream);
+    } else {
+        const ConfigEntry &c = R.table[plan.config_id];
+        TileParams p;
+        p.A = A;
+        p.B = B;
+        p.M = M;
+        p.N = N;
+        p.K = K;
+        p.L = L;
+        p.tiles_m = plan.tiles_m;
+        p.tiles_n = plan.tiles_n;
+        p.split = plan.S;
+        p.chunks_per_split = plan.chunks_per_split;
+        p.total_chunks = plan.total_chunks;
+        if (plan.S == 1) {
+            p.C = C;
+            e = c.fn[plan.P][epilogue](p, (int)plan.grid, stream);
+        } else {
+            void *ws = nullptr;
+            if (o && o->workspace) {
+                if (o->workspace_bytes < plan.ws_bytes) return GEMM_MKL_STATUS_WORKSPACE;
+                ws = o->workspace;
+            } else {
+                st = get_workspace(stream, plan.ws_bytes, &ws);
+                if (st != GEMM_MKL_STATUS_OK) return st;
+            }
+            p.C = ws;
+            e = c.fn[plan.P][MODE_PARTIAL](p, (int)plan.grid, stream);
+            if (e == hipSuccess)
+                e = R.k[dtype].reduce[epilogue](reinterpret_cast<const float *>(ws), C, L * M * N, plan.S, stream);
+        }
+    }
+    if (e != hipSuccess) {
+        t_last_hip = e;
+        return GEMM_MKL_STATUS_HIP_ERROR;
+    }
+    return GEMM_MKL_STATUS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void gemm_mkl_opts_init(gemm_mkl_opts *o)
+{
+    if (!o) return;
+    std::memset(o, 0, sizeof(*o));
+    o->prefetch_stages = -1;
+    o->split_k = 0;
+    o->config_id = -1;
+}
+
+int gemm_mkl(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int64_t L, int dtype,
+             int epilogue, void *stream)
+{
+    return run(A, B, C, M, N, K, L, dtype, epilogue, stream, nullptr);
+}
+
+int gemm_mkl_ex(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int64_t L, int dtype,
+                int epilogue, void *stream, const gemm_mkl_opts *opts)
+{
+    return run(A, B, C, M, N, K, L, dtype, epilogue, stream, opts);
+}
+
+int gemm_mkl_get_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, int epilogue,
+                      const gemm_mkl_opts *opts, gemm_mkl_plan *out)
+{
+    int st = check_args(M, N, K, L, dtype, epilogue, opts);
+    if (st != GEMM_MKL_STATUS_OK) return st;
+    if (!out) return GEMM_MKL_STATUS_INVALID_VALUE;
+    std::memset(out, 0, sizeof(*out));
+    if (M == 0 || N == 0 || L == 0) {
+        out->config_id = -1;
+        out->split_k = 1;
+        return GEMM_MKL_STATUS_OK;
+    }
+    Plan plan;
+    st = make_plan(M, N, K, L, dtype, opts, true, &plan);
+    if (st != GEMM_MKL_STATUS_OK) return st;
+    out->config_id = plan.config_id;
+    out->prefetch_stages = plan.P;
+    out->split_k = plan.S;
+    out->general = plan.general ? 1 : 0;
+    out->grid = plan.grid;
+    if (plan.general) {
+        out->block_m = 64;
+        out->block_n = 64;
+        out->block_k = 16;
+        out->threads = 256;
+    } else {
+        const ConfigEntry &c = registry().table[plan.config_id];
+        out->block_m = c.bm;
+        out->block_n = c.bn;
+        out->block_k = 128 / elem_bytes(dtype);
+        out->threads = c.waves_m * c.waves_n * 64;
+    }
+    out->workspace_bytes = plan.ws_bytes;
+    return GEMM_MKL_STATUS_OK;
+}
+
+size_t gemm_mkl_workspace_size(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, int split_k)
+{
+    gemm_mkl_opts o;
+    gemm_mkl_opts_init(&o);
+    o.split_k = split_k;
+    gemm_mkl_plan p;
+    if (gemm_mkl_get_plan(M, N, K, L, dtype, GEMM_MKL_EPI_IDENTITY, &o, &p) != GEMM_MKL_STATUS_OK) return 0;
+    return p.workspace_bytes;
+}
+
+int gemm_mkl_release_workspace(void)
+{
+    std::lock_guard<std::mutex> g(g_ws_mutex);
+    int st = GEMM_MKL_STATUS_OK;
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    for (auto &kv : g_ws) {
+        if (kv.second.ptr) {
+            hipError_t e = hipSetDevice(kv.first.first);
+            if (e == hipSuccess) e = hipFree(kv.second.ptr);
+            if (e != hipSuccess) {
+                t_last_hip = e;
+                st = GEMM_MKL_STATUS_HIP_ERROR;
+            }
+        }
+    }
+    g_ws.clear();
+    (void)hipSetDevice(cur);
+    return st;
+}
+
+const char *gemm_mkl_status_string(int status)
+{
+    switch (status) {
+    case GEMM_MKL_STATUS_OK: return "success";
+    case GEMM_MKL_STATUS_INVALID_VALUE:
+        return "invalid value: null pointer for a non-empty problem, negative or overflowing size, "
+               "misaligned pointer, or an invalid option (prefetch_stages must be -1 (auto) or >= 0)";
+    case GEMM_MKL_STATUS_UNSUPPORTED_DTYPE: return "unsupported dtype: expected GEMM_MKL_F32, GEMM_MKL_F16 or GEMM_MKL_BF16";
+    case GEMM_MKL_STATUS_UNSUPPORTED_EPILOGUE:
+        return "unsupported epilogue: expected GEMM_MKL_EPI_IDENTITY, GEMM_MKL_EPI_RELU or GEMM_MKL_EPI_SILU";
+    case GEMM_MKL_STATUS_WORKSPACE: return "split-K workspace too small or could not be allocated";
+    case GEMM_MKL_STATUS_HIP_ERROR:
+        std::snprintf(t_hip_msg, sizeof t_hip_msg, "HIP error: %s", hipGetErrorString(t_last_hip));
+        return t_hip_msg;
+    case GEMM_MKL_STATUS_NOT_AVAILABLE:
+        return "not available: the forced configuration, prefetch depth or split does not exist or does not fit";
+    default: return "unknown status";
+    }
+}
+
+int gemm_mkl_num_configs(void) { return (int)registry().table.size(); }
+
+const char *gemm_mkl_config_name(int id)
+{
+    Registry &R = registry();
+    if (id < 0 || id >= (int)R.table.size()) return nullptr;
+    return R.table[id].name;
+}
+
+int gemm_mkl_version(void) { return 100; }
+
+}  // extern "C"
