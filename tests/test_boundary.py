@@ -142,7 +142,7 @@ def test_plans_of_the_workloads(lib, key):
     assert p["general"] == 0
     tiles = -(-w.M // p["block_m"]) * -(-w.N // p["block_n"]) * w.L
     assert p["grid"] == tiles * p["split_k"]
-    assert p["block_k"] * (4 if w.dtype == "f32" else 2) == 128
+    assert p["block_k"] * (4 if w.dtype == "f32" else 2) in (64, 128)
     if p["split_k"] > 1:
         assert p["workspace_bytes"] == p["split_k"] * w.L * w.M * w.N * 4
     else:

@@ -22,6 +22,8 @@ typedef hipError_t (*GeneralLaunchFn)(const void *A, const void *B, void *C, int
 struct ConfigEntry {
     int dtype;             // GEMM_MKL_F32 / F16 / BF16
     int bm, bn;            // output tile
+    int rb;                // bytes of K per row in one chunk (64 or 128)
+    int mf;                // MFMA block edge (16 or 32)
     int waves_m, waves_n;  // wave grid (64 lanes each)
     int default_p;         // prefetch_stages used when not forced
     const char *name;
@@ -40,35 +42,39 @@ void register_bf16(std::vector<ConfigEntry> &table, DtypeKernels &k);
 
 // ---------------------------------------------------------------- helpers for the units
 
-template <class T, int BM, int BN, int WMW, int WNW, int P, int MODE>
+template <class T, int BM, int BN, int RB, int WMW, int WNW, int MF, int P, int MODE>
 hipError_t launch_tile(const TileParams &p, int grid, hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemm_tile_kernel<T, BM, BN, WMW, WNW, P, MODE>), dim3(grid), dim3(WMW * WNW * 64), 0,
-                       stream, p);
+    hipLaunchKernelGGL((gemm_tile_kernel<T, BM, BN, RB, WMW, WNW, MF, P, MODE>), dim3(grid), dim3(WMW * WNW * 64),
+                       0, stream, p);
     return hipGetLastError();
 }
 
-template <class T, int BM, int BN, int WMW, int WNW, int P>
+template <class T, int BM, int BN, int RB, int WMW, int WNW, int MF, int P>
 void fill_prefetch(ConfigEntry &e)
 {
-    e.fn[P][MODE_IDENTITY] = &launch_tile<T, BM, BN, WMW, WNW, P, MODE_IDENTITY>;
-    e.fn[P][MODE_RELU] = &launch_tile<T, BM, BN, WMW, WNW, P, MODE_RELU>;
-    e.fn[P][MODE_SILU] = &launch_tile<T, BM, BN, WMW, WNW, P, MODE_SILU>;
-    e.fn[P][MODE_PARTIAL] = &launch_tile<T, BM, BN, WMW, WNW, P, MODE_PARTIAL>;
+    e.fn[P][MODE_IDENTITY] = &launch_tile<T, BM, BN, RB, WMW, WNW, MF, P, MODE_IDENTITY>;
+    e.fn[P][MODE_RELU] = &launch_tile<T, BM, BN, RB, WMW, WNW, MF, P, MODE_RELU>;
+    e.fn[P][MODE_SILU] = &launch_tile<T, BM, BN, RB, WMW, WNW, MF, P, MODE_SILU>;
+    e.fn[P][MODE_PARTIAL] = &launch_tile<T, BM, BN, RB, WMW, WNW, MF, P, MODE_PARTIAL>;
 }
 
-template <class T, int BM, int BN, int WMW, int WNW, int... Ps>
+// A configuration: tile BM x BN, RB bytes of K per row and chunk, a WMW x WNW
+// wave grid, MFMA edge MF, instantiated for prefetch depths Ps.
+template <class T, int BM, int BN, int RB, int WMW, int WNW, int MF, int... Ps>
 ConfigEntry make_entry(int dtype, int default_p, const char *name)
 {
     ConfigEntry e{};
     e.dtype = dtype;
     e.bm = BM;
     e.bn = BN;
+    e.rb = RB;
+    e.mf = MF;
     e.waves_m = WMW;
     e.waves_n = WNW;
     e.default_p = default_p;
     e.name = name;
-    (fill_prefetch<T, BM, BN, WMW, WNW, Ps>(e), ...);
+    (fill_prefetch<T, BM, BN, RB, WMW, WNW, MF, Ps>(e), ...);
     return e;
 }
 

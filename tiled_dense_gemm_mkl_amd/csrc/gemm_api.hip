@@ -12,6 +12,7 @@
 
 #include <cstdio>
 #include <cstdlib>
+#include <algorithm>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -71,7 +72,7 @@ struct Plan {
     int S = 1;
     bool general = false;
     int64_t grid = 0;
-    int32_t tiles_m = 0, tiles_n = 0;
+    int32_t tiles_m = 0, tiles_n = 0, group_m = 1;
     int32_t total_chunks = 0, chunks_per_split = 0;
     size_t ws_bytes = 0;
 };
@@ -102,21 +103,23 @@ int check_args(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, int epilog
 }
 
 // Modelled time of one configuration, in cycles of one CU, for the heuristic.
-double model_cycles(const ConfigEntry &c, int dtype, int64_t M, int64_t N, int64_t K, int64_t L, int S,
-                    int total_chunks)
+double model_cycles(const ConfigEntry &c, int dtype, int64_t M, int64_t N, int64_t K, int64_t L, int S)
 {
+    const int total_chunks = (int)((K * elem_bytes(dtype) + c.rb - 1) / c.rb);
     const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn) * L;
     const int64_t units = tiles * S;
     const int64_t rounds = (units + kNumCUs - 1) / kNumCUs;
     const int chunks = (total_chunks + S - 1) / S;
-    const double bk = 128.0 / elem_bytes(dtype);
+    const double bk = (double)c.rb / elem_bytes(dtype);
     const double peak = dtype == GEMM_MKL_F32 ? 256.0 : 4096.0;  // flop / clk / CU
     double eff;
     const int area = c.bm * c.bn;
     if (dtype == GEMM_MKL_F32)
         eff = area >= 128 * 128 ? 0.8 : (area >= 64 * 64 ? 0.7 : 0.5);
+    else if (c.mf == 16)
+        eff = 0.3;
     else
-        eff = area >= 256 * 128 ? 0.75 : (area >= 128 * 128 ? 0.65 : 0.3);
+        eff = area >= 256 * 256 ? 0.85 : (area >= 256 * 128 ? 0.75 : (area >= 128 * 128 ? 0.6 : 0.3));
     const double per_chunk = 2.0 * c.bm * c.bn * bk / (peak * eff) + 60.0;
     double cyc = (double)rounds * (chunks * per_chunk + 1500.0);
     if (S > 1) {
@@ -131,9 +134,10 @@ bool fast_path_ok(const ConfigEntry &c, int dtype, int64_t K)
 {
     const int64_t es = elem_bytes(dtype);
     if ((K * es) % 16 != 0) return false;
-    // offsets inside one tile's buffer resource must stay below 2^31
-    if (((int64_t)c.bm + 1) * K * es + 256 >= (int64_t)kOutOfRange) return false;
-    if (((int64_t)c.bn + 1) * K * es + 256 >= (int64_t)kOutOfRange) return false;
+    // offsets inside one tile's buffer resource (which starts kRsrcBias bytes
+    // before the tile) must stay below 2^31
+    if (((int64_t)c.bm + 1) * K * es + 2 * kRsrcBias + 256 >= (int64_t)kOutOfRange) return false;
+    if (((int64_t)c.bn + 1) * K * es + 2 * kRsrcBias + 256 >= (int64_t)kOutOfRange) return false;
     return true;
 }
 
@@ -155,9 +159,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
     if (forced_p > kMaxPrefetch) return GEMM_MKL_STATUS_NOT_AVAILABLE;
     if (forced_s > kMaxSplit) return GEMM_MKL_STATUS_NOT_AVAILABLE;
 
-    const int64_t total_chunks64 = (K * es + 127) / 128;
-    if (total_chunks64 > INT32_MAX) return GEMM_MKL_STATUS_NOT_AVAILABLE;
-    const int total_chunks = (int)total_chunks64;
+    if ((K * es + 63) / 64 > INT32_MAX) return GEMM_MKL_STATUS_NOT_AVAILABLE;
 
     bool general = force_general || !ptrs_aligned;
     if (!general) {
@@ -194,12 +196,13 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
         if (!fast_path_ok(c, dtype, K)) continue;
         const int p = forced_p >= 0 ? forced_p : c.default_p;
         if (c.fn[p][0] == nullptr) continue;
+        const int total_chunks = (int)((K * es + c.rb - 1) / c.rb);
         for (int S = 1; S <= kMaxSplit; ++S) {
             if (forced_s > 0 && S != forced_s) continue;
             if (forced_s <= 0 && S > 1 && (total_chunks + S - 1) / S < 4) break;
             if (forced_s <= 0 && S != 1 && S != 2 && S != 3 && S != 4 && S != 6 && S != 8 && S != 12 && S != 16)
                 continue;
-            const double cyc = model_cycles(c, dtype, M, N, K, L, S, total_chunks);
+            const double cyc = model_cycles(c, dtype, M, N, K, L, S);
             if (cyc < best) {
                 best = cyc;
                 best_c = id;
@@ -209,6 +212,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
     }
     if (best_c < 0) return GEMM_MKL_STATUS_NOT_AVAILABLE;
     const ConfigEntry &c = R.table[best_c];
+    const int total_chunks = (int)((K * es + c.rb - 1) / c.rb);
     plan->general = false;
     plan->config_id = best_c;
     plan->P = forced_p >= 0 ? forced_p : c.default_p;
@@ -224,6 +228,10 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
         if (used < 1) used = 1;
         plan->S = used;
     }
+    // raster groups of up to 4 tile rows: the 32 workgroups an XCD runs at
+    // once then share few A row-blocks and B column-blocks in its L2
+    plan->group_m = std::min<int32_t>(plan->tiles_m, (int32_t)env_int("GEMM_MKL_GROUP_M", 4));
+    if (plan->group_m < 1) plan->group_m = 1;
     plan->grid = (int64_t)plan->tiles_m * plan->tiles_n * plan->S * L;
     if (plan->grid > INT32_MAX) return GEMM_MKL_STATUS_NOT_AVAILABLE;
     plan->ws_bytes = plan->S > 1 ? (size_t)plan->S * (size_t)(L * M * N) * 4 : 0;
@@ -316,6 +324,7 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
         p.L = L;
         p.tiles_m = plan.tiles_m;
         p.tiles_n = plan.tiles_n;
+        p.group_m = plan.group_m;
         p.split = plan.S;
         p.chunks_per_split = plan.chunks_per_split;
         p.total_chunks = plan.total_chunks;
@@ -398,7 +407,7 @@ int gemm_mkl_get_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, int
         const ConfigEntry &c = registry().table[plan.config_id];
         out->block_m = c.bm;
         out->block_n = c.bn;
-        out->block_k = 128 / elem_bytes(dtype);
+        out->block_k = c.rb / elem_bytes(dtype);
         out->threads = c.waves_m * c.waves_n * 64;
     }
     out->workspace_bytes = plan.ws_bytes;

@@ -48,10 +48,6 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 enum Mode { MODE_IDENTITY = 0, MODE_RELU = 1, MODE_SILU = 2, MODE_PARTIAL = 3 };
 
-// Bytes of one staged row of a chunk, and of one MFMA k-step per row.
-constexpr int kRowBytes = 128;
-constexpr int kStepBytes = 64;
-constexpr int kStepsPerChunk = kRowBytes / kStepBytes;
 // A voffset at or above every buffer's num_records: the load returns zeros.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
@@ -61,9 +57,10 @@ struct TileParams {
     void *C;          // output (modes 0..2) or fp32 workspace [S][L][M][N] (partial)
     int64_t M, N, K, L;
     int32_t tiles_m, tiles_n;
+    int32_t group_m;          // tile rows per raster group (L2 reuse)
     int32_t split;            // S
-    int32_t chunks_per_split; // chunks of kRowBytes per split (the last may be short)
-    int32_t total_chunks;     // ceil(K * elem / kRowBytes)
+    int32_t chunks_per_split; // K chunks per split (the last split may be short)
+    int32_t total_chunks;     // ceil(K * elem / row bytes of a chunk)
 };
 
 // ------------------------------------------------------------------ epilogue
@@ -155,20 +152,48 @@ __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t num_record
     return r;
 }
 
-// One direct global->LDS load of 16 bytes per lane: lane t writes LDS bytes
-// [lds_base + 16 t, lds_base + 16 t + 16).  The LDS base goes in M0.  It is
-// written as inline asm so that the compiler does not add conservative waits
-// for it; the ring below waits on vmcnt explicitly.  A write of M0 needs one
-// wait state before an LDS-DMA instruction reads it, hence the s_nop.
-__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_base, uint32_t voffset, uint32_t soffset)
+// Direct global->LDS loads of 16 bytes per lane.  Lane t of a load writes LDS
+// bytes [M0 + OFF + 16 t, M0 + OFF + 16 t + 16) with the 16 global bytes at
+// rsrc.base + voffset + soffset + OFF; the instruction offset OFF (0, 1024,
+// 2048 or 3072 here) moves both addresses.  Writing M0 costs far more than the
+// load itself, so one M0 value serves four consecutive 1 KB blocks.  The loads
+// are inline asm so that the compiler adds no conservative waits for them;
+// the ring waits on vmcnt explicitly.  A write of M0 needs one wait state
+// before an LDS-DMA instruction reads it, hence the s_nop.
+__device__ __forceinline__ void dma16_set_m0(i32x4 rsrc, uint32_t m0, uint32_t voffset, uint32_t soffset)
 {
     asm volatile("s_mov_b32 m0, %0\n\t"
                  "s_nop 0\n\t"
                  "buffer_load_dwordx4 %1, %2, %3 offen lds"
                  :
-                 : "s"(lds_base), "v"(voffset), "s"(rsrc), "s"(soffset)
+                 : "s"(m0), "v"(voffset), "s"(rsrc), "s"(soffset)
                  : "memory");
 }
+
+// Load block j (1..3) of the four sharing the current M0.
+__device__ __forceinline__ void dma16_same_m0(i32x4 rsrc, int j, uint32_t voffset, uint32_t soffset)
+{
+    switch (j) {
+    case 1:
+        asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:1024 lds" : : "v"(voffset), "s"(rsrc), "s"(soffset)
+                     : "memory");
+        break;
+    case 2:
+        asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:2048 lds" : : "v"(voffset), "s"(rsrc), "s"(soffset)
+                     : "memory");
+        break;
+    default:
+        asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:3072 lds" : : "v"(voffset), "s"(rsrc), "s"(soffset)
+                     : "memory");
+        break;
+    }
+}
+
+// The global side of a block j load gets OFF = (j % 4) * 1024 added; the
+// resource base sits kRsrcBias bytes before the tile and every voffset carries
+// kRsrcBias - OFF, so the byte read is exactly the intended one and voffset
+// never goes negative.
+constexpr uint32_t kRsrcBias = 4096;
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
@@ -210,24 +235,88 @@ __device__ __forceinline__ int xcd_remap(int wg, int grid)
 
 // ------------------------------------------------------------------ the tiled kernel
 
-template <class T, int BM, int BN, int WAVES_M, int WAVES_N, int P, int MODE>
+// LDS row layout of one chunk: RB bytes per row (64 or 128), split in 16-byte
+// columns.  Column c of row r is stored at physical column c ^ swizzle(r):
+//   RB = 128 (8 columns): swizzle(r) = (r & 7) ^ ((r >> 3) & 1)
+//   RB =  64 (4 columns): swizzle(r) = (r >> 2) & 3
+// In both cases 16 consecutive rows read at one logical column land on 16
+// distinct 16-byte bank groups of a 256-byte bank row (and 8 consecutive rows
+// on 8 distinct groups of a 128-byte bank row).
+template <int RB>
+__device__ __forceinline__ int row_swizzle(int r)
+{
+    if constexpr (RB == 128)
+        return (r & 7) ^ ((r >> 3) & 1);
+    else
+        return (r >> 2) & 3;
+}
+
+template <class T, int MF> struct Mfma;
+
+template <class T> struct Mfma<T, 16> {
+    typedef f32x4 acc_t;
+    static constexpr int regs = 4;
+    __device__ static __forceinline__ acc_t step(i32x4 a, i32x4 b, acc_t c) { return Elem<T>::mfma_step(a, b, c); }
+};
+
+template <class T> struct Mfma<T, 32> {
+    typedef float acc_t __attribute__((ext_vector_type(16)));
+    static constexpr int regs = 16;
+    __device__ static __forceinline__ acc_t step(i32x4 a, i32x4 b, acc_t c)
+    {
+        if constexpr (sizeof(T) == 4) {
+            // 16 bytes = 4 consecutive k of a row: four 32x32x2 MFMAs, MFMA j taking
+            // component j on both operands
+            f32x4v av = __builtin_bit_cast(f32x4v, a);
+            f32x4v bv = __builtin_bit_cast(f32x4v, b);
+            c = __builtin_amdgcn_mfma_f32_32x32x2f32(av[0], bv[0], c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_32x32x2f32(av[1], bv[1], c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_32x32x2f32(av[2], bv[2], c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_32x32x2f32(av[3], bv[3], c, 0, 0, 0);
+            return c;
+        } else if constexpr (__is_same(T, __bf16)) {
+            return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                           c, 0, 0, 0);
+        } else {
+            return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                          c, 0, 0, 0);
+        }
+    }
+};
+
+// One workgroup computes a BM x BN tile of C (or of a split-K partial).
+//   RB      bytes of K per row in one chunk (the K-outer step)
+//   MF      MFMA block edge: 32 (v_mfma_f32_32x32x16 / 32x32x2f32) or 16
+//   P       prefetch_stages: chunks in flight ahead of the one consumed
+//   MODE    epilogue (identity / ReLU / SiLU) or split-K partial store
+template <class T, int BM, int BN, int RB, int WAVES_M, int WAVES_N, int MF, int P, int MODE>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_tile_kernel(TileParams p)
 {
+    typedef Mfma<T, MF> MM;
+    typedef typename MM::acc_t acc_t;
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int ES = Elem<T>::bytes;
+    constexpr int NCH = RB / 16;                  // 16-byte columns per row
+    constexpr int ROWS_PER_LOAD = 1024 / RB;      // rows covered by one 64-lane 16-byte load
     constexpr int WTM = BM / WAVES_M;
     constexpr int WTN = BN / WAVES_N;
-    constexpr int FM = WTM / 16;
-    constexpr int FN = WTN / 16;
+    constexpr int FM = WTM / MF;
+    constexpr int FN = WTN / MF;
+    constexpr int STEP_COLS = 64 / MF;            // 16-byte columns one MFMA k-step reads per row
+    constexpr int KSTEPS = NCH / STEP_COLS;
+    constexpr int LANE_ROWS = MF;                 // rows covered by one operand read (lanes mod MF)
     constexpr int SLOTS = P + 1;
-    constexpr int SLOT_BYTES = (BM + BN) * kRowBytes;
-    constexpr int A_GROUPS = BM / 8;              // 8 rows x 128 B = one wave load
-    constexpr int B_GROUPS = BN / 8;
-    constexpr int A_LOADS = A_GROUPS / NW;        // loads per wave per chunk
+    constexpr int SLOT_BYTES = (BM + BN) * RB;
+    constexpr int A_GROUPS = BM / ROWS_PER_LOAD;
+    constexpr int B_GROUPS = BN / ROWS_PER_LOAD;
+    constexpr int A_LOADS = A_GROUPS / NW;
     constexpr int B_LOADS = B_GROUPS / NW;
     constexpr int LOADS = A_LOADS + B_LOADS;
-    static_assert(BM % (16 * WAVES_M) == 0 && BN % (16 * WAVES_N) == 0, "wave tile");
+    static_assert(RB == 64 || RB == 128, "row bytes");
+    static_assert(MF == 16 || MF == 32, "MFMA shape");
+    static_assert(BM % (MF * WAVES_M) == 0 && BN % (MF * WAVES_N) == 0, "wave tile");
     static_assert(A_GROUPS % NW == 0 && B_GROUPS % NW == 0, "load split");
+    static_assert(KSTEPS >= 2 && KSTEPS % 2 == 0, "k-steps per chunk: even, for the register double buffer");
     static_assert(SLOTS * SLOT_BYTES <= 160 * 1024, "LDS budget of a gfx950 workgroup");
     static_assert(LOADS * (P > 0 ? P : 1) < 64, "vmcnt range");
 
@@ -236,15 +325,19 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_tile_kernel(TilePa
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-    // ---- tile mapping: [l][s][tile_n][tile_m], tile_m fastest
-    const int grid = gridDim.x;
-    int t = xcd_remap(blockIdx.x, grid);
-    const int tm = t % p.tiles_m;
-    t /= p.tiles_m;
-    const int tn = t % p.tiles_n;
-    t /= p.tiles_n;
+    // ---- tile mapping: [l][s][tile], tiles rastered in groups of group_m tile
+    // rows (column-major inside a group), after the XCD remap
+    int t = xcd_remap(blockIdx.x, gridDim.x);
+    const int tiles = p.tiles_m * p.tiles_n;
+    const int tile = t % tiles;
+    t /= tiles;
     const int s = t % p.split;
     const int l = t / p.split;
+    const int width = p.group_m * p.tiles_n;
+    const int first_m = (tile / width) * p.group_m;
+    const int gsize = min(p.tiles_m - first_m, p.group_m);
+    const int tm = first_m + (tile % width) % gsize;
+    const int tn = (tile % width) / gsize;
 
     const int64_t m0 = (int64_t)tm * BM;
     const int64_t n0 = (int64_t)tn * BN;
@@ -261,152 +354,240 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_tile_kernel(TilePa
     const int64_t rows_b = p.N - n0;
     const int64_t bytes_a = rows_a * K * ES;
     const int64_t bytes_b = rows_b * K * ES;
-    const i32x4 rsrc_a = make_rsrc(Ab, (uint32_t)(bytes_a < (int64_t)kOutOfRange ? bytes_a : kOutOfRange));
-    const i32x4 rsrc_b = make_rsrc(Bb, (uint32_t)(bytes_b < (int64_t)kOutOfRange ? bytes_b : kOutOfRange));
+    // the descriptors start kRsrcBias bytes early (see dma16_same_m0); nothing
+    // is ever read there, and the range check still ends at the tile's last row
+    const int64_t lim_a = bytes_a + kRsrcBias, lim_b = bytes_b + kRsrcBias;
+    const i32x4 rsrc_a = make_rsrc(reinterpret_cast<const char *>(Ab) - kRsrcBias,
+                                   (uint32_t)(lim_a < (int64_t)kOutOfRange ? lim_a : kOutOfRange));
+    const i32x4 rsrc_b = make_rsrc(reinterpret_cast<const char *>(Bb) - kRsrcBias,
+                                   (uint32_t)(lim_b < (int64_t)kOutOfRange ? lim_b : kOutOfRange));
 
-    // ---- per-lane load offsets: lane -> (row r = lane/8 of the group, physical column lane%8)
-    // The logical 16-byte column held at physical column c of row r is c ^ swz(r).
+    // ---- per-lane load offsets.  Wave w loads the row groups
+    // [w * A_LOADS, (w + 1) * A_LOADS) of A (and likewise of B), so that its
+    // blocks are contiguous in LDS; lane -> (row lane / NCH of the group,
+    // physical column lane % NCH, holding logical column that ^ swizzle(row)).
     uint32_t voff_a[A_LOADS], voff_b[B_LOADS];
     int col_a[A_LOADS], col_b[B_LOADS];
     const int64_t row_bytes_g = K * ES;
 #pragma unroll
     for (int j = 0; j < A_LOADS; ++j) {
-        const int g = wave + j * NW;
-        const int r = g * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ swz(r);
+        const int g = wave * A_LOADS + j;
+        const int r = g * ROWS_PER_LOAD + lane / NCH;
+        const int c = (lane % NCH) ^ row_swizzle<RB>(r);
         col_a[j] = c;
-        voff_a[j] = (r < rows_a) ? (uint32_t)(r * row_bytes_g + c * 16) : kOutOfRange;
+        voff_a[j] = (r < rows_a) ? (uint32_t)(r * row_bytes_g + c * 16 + kRsrcBias - (j & 3) * 1024) : kOutOfRange;
     }
 #pragma unroll
     for (int j = 0; j < B_LOADS; ++j) {
-        const int g = wave + j * NW;
-        const int r = g * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ swz(r);
+        const int g = wave * B_LOADS + j;
+        const int r = g * ROWS_PER_LOAD + lane / NCH;
+        const int c = (lane % NCH) ^ row_swizzle<RB>(r);
         col_b[j] = c;
-        voff_b[j] = (r < rows_b) ? (uint32_t)(r * row_bytes_g + c * 16) : kOutOfRange;
+        voff_b[j] = (r < rows_b) ? (uint32_t)(r * row_bytes_g + c * 16 + kRsrcBias - (j & 3) * 1024) : kOutOfRange;
     }
     const uint32_t smem_base = lds_addr(smem);
     const int64_t k_bytes = K * ES;
 
-    auto issue = [&](int chunk, int slot) {
-        const int64_t kb = (int64_t)(chunk0 + chunk) * kRowBytes;   // byte offset of the chunk in a row
-        const int64_t rem = k_bytes - kb;                            // bytes of this row left from kb
+    // Load q (0 <= q < LOADS) of one chunk: q < A_LOADS are A row groups, the
+    // rest B row groups.  Every wave issues the same number of loads per chunk,
+    // which is what the vmcnt waits below count.
+    auto issue_one = [&](int chunk, int slot, int q) {
+        const int64_t kb = (int64_t)(chunk0 + chunk) * RB;   // byte offset of the chunk in a row
+        const int64_t rem = k_bytes - kb;                     // bytes of the row left from kb
         const uint32_t soff = (uint32_t)kb;
         const uint32_t sbase = smem_base + slot * SLOT_BYTES;
-#pragma unroll
-        for (int j = 0; j < A_LOADS; ++j) {
-            const int g = wave + j * NW;
-            uint32_t v = (col_a[j] * 16 < rem) ? voff_a[j] : kOutOfRange;
-            dma16(rsrc_a, sbase + g * 1024, v, soff);
-        }
-#pragma unroll
-        for (int j = 0; j < B_LOADS; ++j) {
-            const int g = wave + j * NW;
-            uint32_t v = (col_b[j] * 16 < rem) ? voff_b[j] : kOutOfRange;
-            dma16(rsrc_b, sbase + BM * kRowBytes + g * 1024, v, soff);
+        if (q < A_LOADS) {
+            const int j = q;
+            const uint32_t v = (col_a[j] * 16 < rem) ? voff_a[j] : kOutOfRange;
+            if ((j & 3) == 0)
+                dma16_set_m0(rsrc_a, sbase + (wave * A_LOADS + j) * 1024, v, soff);
+            else
+                dma16_same_m0(rsrc_a, j & 3, v, soff);
+        } else {
+            const int j = q - A_LOADS;
+            const uint32_t v = (col_b[j] * 16 < rem) ? voff_b[j] : kOutOfRange;
+            if ((j & 3) == 0)
+                dma16_set_m0(rsrc_b, sbase + BM * RB + (wave * B_LOADS + j) * 1024, v, soff);
+            else
+                dma16_same_m0(rsrc_b, j & 3, v, soff);
         }
     };
+    auto issue = [&](int chunk, int slot) {
+#pragma unroll
+        for (int q = 0; q < LOADS; ++q) issue_one(chunk, slot, q);
+    };
 
-    // ---- operand read offsets (within a slot)
+    // ---- operand reads: lane reads row (lane % MF) of each fragment at logical
+    // column ks * STEP_COLS + lane / MF
     const int wm = wave % WAVES_M;
     const int wn = wave / WAVES_M;
-    const int r16 = lane & 15;
-    const int grp = lane >> 4;
-    const int sw = swz(r16);
-    uint32_t rd_a = (uint32_t)((wm * WTM + r16) * kRowBytes);
-    uint32_t rd_b = (uint32_t)(BM * kRowBytes + (wn * WTN + r16) * kRowBytes);
+    const int lrow = lane % LANE_ROWS;
+    const int lcol = lane / LANE_ROWS;
+    const int sw = row_swizzle<RB>(lrow);
+    const uint32_t rd_a = (uint32_t)((wm * WTM + lrow) * RB);
+    const uint32_t rd_b = (uint32_t)(BM * RB + (wn * WTN + lrow) * RB);
 
-    f32x4 acc[FM][FN];
+    acc_t acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-            acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int q = 0; q < MM::regs; ++q)
+                acc[i][j][q] = 0.0f;
 
-    auto compute = [&](int slot) {
+    // operand fragments, double-buffered in registers: the reads for k-step
+    // ks + 1 are issued between the MFMAs of k-step ks
+    constexpr int NMF = FM * FN;                  // MFMAs per k-step
+    constexpr int NRD = FM + FN;                  // fragment reads per k-step
+    i32x4 fa[2][FM], fb[2][FN];
+    auto read_one = [&](int slot, int ks, int buf, int r) {
         const char *base = smem + slot * SLOT_BYTES;
-#pragma unroll
-        for (int ks = 0; ks < kStepsPerChunk; ++ks) {
-            const int col = ((ks * 4 + grp) ^ sw) * 16;
-            i32x4 fa[FM], fb[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-                fa[i] = *reinterpret_cast<const i32x4 *>(base + rd_a + i * 16 * kRowBytes + col);
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                fb[j] = *reinterpret_cast<const i32x4 *>(base + rd_b + j * 16 * kRowBytes + col);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = Elem<T>::mfma_step(fb[j], fa[i], acc[i][j]);
-        }
+        const int col = ((ks * STEP_COLS + lcol) ^ sw) * 16;
+        if (r < FM)
+            fa[buf][r] = *reinterpret_cast<const i32x4 *>(base + rd_a + r * MF * RB + col);
+        else
+            fb[buf][r - FM] = *reinterpret_cast<const i32x4 *>(base + rd_b + (r - FM) * MF * RB + col);
+    };
+    auto mfma_one = [&](int buf, int t) {
+        const int i = t / FN, j = t % FN;
+        acc[i][j] = MM::step(fb[buf][j], fa[buf][i], acc[i][j]);
     };
 
-    // ---- the prefetch ring
     if constexpr (P == 0) {
         for (int i = 0; i < nk; ++i) {
             lds_barrier();                 // everyone is done reading the single slot
             issue(i, 0);
             wait_vmcnt<0>();
             lds_barrier();                 // every wave's part of chunk i has landed
-            compute(0);
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+                for (int r = 0; r < NRD; ++r) read_one(0, ks, ks & 1, r);
+#pragma unroll
+                for (int t = 0; t < NMF; ++t) mfma_one(ks & 1, t);
+            }
         }
     } else {
+        // The ring.  During iteration i (consuming chunk i from slot i mod
+        // SLOTS) the loads of chunk i + P go to slot (i + P) mod SLOTS, the slot
+        // chunk i - 1 used, spread between the MFMAs.  At the end of iteration i
+        // chunk i + 1 is waited for, a barrier makes every wave's part of it
+        // visible and retires every wave's reads of chunk i, and the first
+        // fragments of chunk i + 1 are read under the last MFMAs of chunk i.
+        constexpr int LPK = (LOADS + KSTEPS - 1) / KSTEPS;        // loads per k-step
+        constexpr int LGAP = (NMF / LPK) > 0 ? (NMF / LPK) : 1;    // MFMAs between loads
+        constexpr int RGAP = 1;   // reads go right behind the first MFMAs, so they land well before use
 #pragma unroll
-        for (int i = 0; i < P; ++i)
-            if (i < nk) issue(i, i);
-        int slot = 0;
-        for (int i = 0; i < nk; ++i) {
-            // chunks issued after chunk i so far: min(P - 1, nk - 1 - i)
-            if (nk - 1 - i >= P - 1)
+        for (int c = 0; c < P; ++c)
+            if (c < nk) issue(c, c);
+        if (nk > 0) {
+            if (nk - 1 >= P - 1)
                 wait_vmcnt<LOADS * (P - 1)>();
             else
                 wait_vmcnt<0>();
-            lds_barrier();                 // chunk i visible to all; slot (i-1) mod SLOTS free
-            if (i + P < nk) {
-                int ns = slot + P;
-                if (ns >= SLOTS) ns -= SLOTS;
-                issue(i + P, ns);
+            lds_barrier();
+#pragma unroll
+            for (int r = 0; r < NRD; ++r) read_one(0, 0, 0, r);
+        }
+        int slot = 0;
+        int fill = P;                      // slot that receives chunk i + P
+        for (int i = 0; i < nk; ++i) {
+            const int next = (slot + 1 == SLOTS) ? 0 : slot + 1;
+            const bool do_issue = i + P < nk;
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+                const bool last = ks + 1 == KSTEPS;
+                if (last) {
+                    // remaining loads of chunk i + P, then chunk i + 1 must have
+                    // landed: chunks issued after it so far: min(P - 1, nk - 2 - i)
+#pragma unroll
+                    for (int q = ks * LPK; q < LOADS; ++q)
+                        if (do_issue) issue_one(i + P, fill, q);
+                    if (i + 1 < nk) {
+                        if (nk - 2 - i >= P - 1)
+                            wait_vmcnt<LOADS * (P - 1)>();
+                        else
+                            wait_vmcnt<0>();
+                        lds_barrier();
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int t = 0; t < NMF; ++t) {
+                    mfma_one(ks & 1, t);
+                    if (t % RGAP == 0 && t / RGAP < NRD) {
+                        if (!last)
+                            read_one(slot, ks + 1, (ks + 1) & 1, t / RGAP);
+                        else if (i + 1 < nk)
+                            read_one(next, 0, 0, t / RGAP);
+                    }
+                    if (!last && t % LGAP == 0 && t / LGAP < LPK) {
+                        const int q = ks * LPK + t / LGAP;
+                        if (q < LOADS && do_issue) issue_one(i + P, fill, q);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                // reads and loads that did not fit between the MFMAs
+#pragma unroll
+                for (int r = (NMF + RGAP - 1) / RGAP; r < NRD; ++r) {
+                    if (!last)
+                        read_one(slot, ks + 1, (ks + 1) & 1, r);
+                    else if (i + 1 < nk)
+                        read_one(next, 0, 0, r);
+                }
+                if (!last) {
+#pragma unroll
+                    for (int u = (NMF + LGAP - 1) / LGAP; u < LPK; ++u) {
+                        const int q = ks * LPK + u;
+                        if (q < LOADS && do_issue) issue_one(i + P, fill, q);
+                    }
+                }
             }
-            compute(slot);
-            slot = (slot + 1 == SLOTS) ? 0 : slot + 1;
+            slot = next;
+            fill = (fill + 1 == SLOTS) ? 0 : fill + 1;
         }
     }
 
-    // ---- epilogue: lane owns C[m][n..n+3] for every fragment (i, j)
+    // ---- epilogue.  With the operands swapped, fragment (i, j) holds C^T:
+    //   MF = 16: value q of lane -> m = lane % 16, n = 4 (lane / 16) + q
+    //   MF = 32: value 4 g + q   -> m = lane % 32, n = 8 g + 4 (lane / 32) + q
     const int64_t M = p.M, N = p.N;
     const bool vec_ok = (N & 3) == 0;
+    constexpr int GROUPS = MM::regs / 4;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-        const int64_t m = m0 + wm * WTM + i * 16 + r16;
+        const int64_t m = m0 + wm * WTM + i * MF + lrow;
         if (m >= M) continue;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            const int64_t n = n0 + wn * WTN + j * 16 + grp * 4;
-            f32x4 v = acc[i][j];
-            if constexpr (MODE == MODE_PARTIAL) {
-                float *W = reinterpret_cast<float *>(p.C) + ((int64_t)s * p.L + l) * M * N + m * N;
-                if (vec_ok && n + 3 < N) {
-                    *reinterpret_cast<f32x4v *>(W + n) = f32x4v{v[0], v[1], v[2], v[3]};
-                } else {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (n + q < N) W[n + q] = v[q];
-                }
-            } else {
-                T *Cr = reinterpret_cast<T *>(p.C) + ((int64_t)l * M + m) * N;
-                const float y0 = apply_epilogue<MODE>(v[0]);
-                const float y1 = apply_epilogue<MODE>(v[1]);
-                const float y2 = apply_epilogue<MODE>(v[2]);
-                const float y3 = apply_epilogue<MODE>(v[3]);
-                if (vec_ok && n + 3 < N) {
-                    Elem<T>::store4(Cr + n, y0, y1, y2, y3);
-                } else {
-                    const float y[4] = {y0, y1, y2, y3};
+            for (int g = 0; g < GROUPS; ++g) {
+                const int64_t n = n0 + wn * WTN + j * MF + g * 8 + lcol * 4;
+                const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
+                const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+                if constexpr (MODE == MODE_PARTIAL) {
+                    float *W = reinterpret_cast<float *>(p.C) + ((int64_t)s * p.L + l) * M * N + m * N;
+                    if (vec_ok && n + 3 < N) {
+                        *reinterpret_cast<f32x4v *>(W + n) = f32x4v{v0, v1, v2, v3};
+                    } else {
+                        const float v[4] = {v0, v1, v2, v3};
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (n + q < N) Cr[n + q] = Elem<T>::from_f32(y[q]);
+                        for (int q = 0; q < 4; ++q)
+                            if (n + q < N) W[n + q] = v[q];
+                    }
+                } else {
+                    T *Cr = reinterpret_cast<T *>(p.C) + ((int64_t)l * M + m) * N;
+                    const float y0 = apply_epilogue<MODE>(v0), y1 = apply_epilogue<MODE>(v1);
+                    const float y2 = apply_epilogue<MODE>(v2), y3 = apply_epilogue<MODE>(v3);
+                    if (vec_ok && n + 3 < N) {
+                        Elem<T>::store4(Cr + n, y0, y1, y2, y3);
+                    } else {
+                        const float y[4] = {y0, y1, y2, y3};
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            if (n + q < N) Cr[n + q] = Elem<T>::from_f32(y[q]);
+                    }
                 }
             }
         }

@@ -8,9 +8,11 @@ void register_f32(std::vector<ConfigEntry> &t, DtypeKernels &k)
 {
     typedef float T;
     const int d = GEMM_MKL_F32;
-    t.push_back(make_entry<T, 64, 64, 2, 2, 0, 1, 2, 3>(d, 2, "f32 64x64 waves2x2 mfma16x16x4"));
-    t.push_back(make_entry<T, 128, 128, 2, 2, 1, 2, 3>(d, 2, "f32 128x128 waves2x2 mfma16x16x4"));
-    t.push_back(make_entry<T, 32, 64, 1, 2, 1, 2, 3>(d, 3, "f32 32x64 waves1x2 mfma16x16x4"));
+    //                  T  BM   BN   RB  waves MF  prefetch depths
+    t.push_back(make_entry<T, 128, 128, 128, 2, 2, 32, 1, 2, 3>(d, 2, "f32 128x128 k32 waves2x2 mfma32"));
+    t.push_back(make_entry<T, 64, 64, 128, 2, 2, 32, 0, 1, 2, 3>(d, 2, "f32 64x64 k32 waves2x2 mfma32"));
+    t.push_back(make_entry<T, 64, 64, 128, 2, 2, 16, 1, 2>(d, 1, "f32 64x64 k32 waves2x2 mfma16"));
+    t.push_back(make_entry<T, 32, 64, 128, 1, 2, 16, 1, 2, 3>(d, 1, "f32 32x64 k32 waves1x2 mfma16"));
     fill_dtype_kernels<T>(k);
 }
 
