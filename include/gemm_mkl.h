@@ -101,18 +101,29 @@ int gemm_mkl(const void *A, const void *B, void *C,
  *   configuration provides is NOT_AVAILABLE.
  * split_k: number of K ranges computed by separate workgroups and summed in
  *   ascending order of range (0 = auto, 1 = no split, at most 16).  Ranges
- *   that would be empty are dropped.
+ *   that would be empty are dropped.  A value >= 1 also rules out the
+ *   stream-K kernel unless GEMM_MKL_OPT_STREAMK is set (with split_k > 1 that
+ *   combination is NOT_AVAILABLE).
  * config_id: index into the kernel configuration table (-1 = auto); see
  *   gemm_mkl_config_name.  A configuration of another dtype is NOT_AVAILABLE.
- * flags: GEMM_MKL_OPT_FORCE_GENERAL selects the general kernel.
- * workspace / workspace_bytes: caller-owned device memory for the split-K
- *   partial sums (NULL = use the library's internal workspace).  It must hold
- *   the plan's workspace_bytes (gemm_mkl_get_plan) and be 256-byte aligned;
- *   too small is GEMM_MKL_STATUS_WORKSPACE.
+ * flags: GEMM_MKL_OPT_FORCE_GENERAL selects the general kernel;
+ *   GEMM_MKL_OPT_STREAMK / GEMM_MKL_OPT_NO_STREAMK force / forbid the stream-K
+ *   kernel (one workgroup per compute unit, each summing an equal share of all
+ *   (tile, K-chunk) units; tiles cut between workgroups are summed in a fixed
+ *   order, so results stay bitwise reproducible).  The automatic plan uses
+ *   stream-K only when GEMM_MKL_STREAMK=-1 is set in the environment.
+ * workspace / workspace_bytes: caller-owned device memory for split-K or
+ *   stream-K partial sums (NULL = use the library's internal workspace).  It
+ *   must hold the plan's workspace_bytes (gemm_mkl_get_plan) and be 256-byte
+ *   aligned; too small is GEMM_MKL_STATUS_WORKSPACE.  A stream-K plan uses its
+ *   first plan.counter_bytes bytes as per-tile counters: they must be zero
+ *   before the first stream-K call with that workspace, and every completed
+ *   call leaves them zero.
  *
  * The environment variables GEMM_MKL_FORCE_CONFIG, GEMM_MKL_STAGES and
  * GEMM_MKL_SPLIT_K supply the same three choices when opts leaves them
- * automatic (for sweeps); GEMM_MKL_LOG=1 prints each call's plan to stderr;
+ * automatic (for sweeps); GEMM_MKL_STREAMK=0/1/-1 never / always / by model
+ * uses stream-K; GEMM_MKL_GROUP_M sets the tile-raster group height; GEMM_MKL_LOG=1 prints each call's plan to stderr;
  * GEMM_MKL_WORKSPACE_LIMIT=<bytes> caps the internal workspace.
  */
 typedef struct gemm_mkl_opts {
@@ -126,7 +137,11 @@ typedef struct gemm_mkl_opts {
 
 /* flags */
 enum {
-    GEMM_MKL_OPT_FORCE_GENERAL = 1 /* use the general (unaligned-capable) kernel */
+    GEMM_MKL_OPT_FORCE_GENERAL = 1, /* use the general (unaligned-capable) kernel */
+    GEMM_MKL_OPT_STREAMK = 2,       /* use the stream-K kernel (NOT_AVAILABLE if no
+                                       configuration of the dtype has one, or with
+                                       split_k > 1) */
+    GEMM_MKL_OPT_NO_STREAMK = 4     /* never use the stream-K kernel */
 };
 
 /* Initialise opts to "all automatic". */
@@ -151,7 +166,9 @@ typedef struct gemm_mkl_plan {
     int32_t general;          /* 1 if the general kernel is used */
     int64_t grid;             /* workgroups of the main kernel */
     int32_t block_m, block_n, block_k, threads;
-    size_t workspace_bytes;   /* 0 when split_k == 1 */
+    size_t workspace_bytes;   /* 0 when split_k == 1 and not stream-K */
+    int32_t streamk;          /* 1 if the stream-K kernel is used (grid = workgroups) */
+    int32_t counter_bytes;    /* stream-K: leading workspace bytes holding counters */
 } gemm_mkl_plan;
 
 int gemm_mkl_get_plan(int64_t M, int64_t N, int64_t K, int64_t L,

@@ -141,9 +141,18 @@ def test_plans_of_the_workloads(lib, key):
     p = gm.get_plan(w.M, w.N, w.K, w.L, code, epi)
     assert p["general"] == 0
     tiles = -(-w.M // p["block_m"]) * -(-w.N // p["block_n"]) * w.L
-    assert p["grid"] == tiles * p["split_k"]
-    assert p["block_k"] * (4 if w.dtype == "f32" else 2) in (64, 128)
-    if p["split_k"] > 1:
+    es = 4 if w.dtype == "f32" else 2
+    assert p["block_k"] * es in (64, 128)
+    if p["streamk"]:
+        chunks = -(-w.K // p["block_k"])
+        need = -(-chunks // 7)
+        assert p["split_k"] == 1 and p["grid"] == max(1, min(256, tiles * chunks // need))
+        assert p["workspace_bytes"] == p["counter_bytes"] + 2 * p["grid"] * p["block_m"] * p["block_n"] * 4
+    else:
+        assert p["grid"] == tiles * p["split_k"]
+    if p["streamk"]:
+        pass
+    elif p["split_k"] > 1:
         assert p["workspace_bytes"] == p["split_k"] * w.L * w.M * w.N * 4
     else:
         assert p["workspace_bytes"] == 0
@@ -178,7 +187,23 @@ def test_every_prefetch_depth_of_a_config_is_plannable(lib):
         assert ok, f"config {name} has no prefetch depth"
 
 
+def test_streamk_plans(lib):
+    # the headline shape leaves 80 of 256 CUs idle with 128x128 tiles: stream-K
+    # spreads its 176 x 32 chunk units evenly
+    p = gm.get_plan(512, 5632, 2048, 1, BF16, RELU, gm.make_opts(streamk=True))
+    assert p["streamk"] == 1 and p["grid"] == 256 and p["split_k"] == 1
+    assert p["counter_bytes"] % 256 == 0 and p["workspace_bytes"] > p["counter_bytes"]
+    p = gm.get_plan(512, 5632, 2048, 1, BF16, RELU, gm.make_opts(streamk=False))
+    assert p["streamk"] == 0
+    o = gm.make_opts()
+    o.flags = 2 | 4  # both forced and forbidden
+    with pytest.raises(gm.GemmMklError) as e:
+        gm.get_plan(64, 64, 64, 1, BF16, ID, o)
+    assert e.value.status == -1
+
+
 def test_ctypes_struct_sizes_match_header(lib):
-    # gemm_mkl_opts: 4 x int32, pointer, size_t ; gemm_mkl_plan: 4 x int32, int64, 4 x int32, size_t
+    # gemm_mkl_opts: 4 x int32, pointer, size_t
+    # gemm_mkl_plan: 4 x int32, int64, 4 x int32, size_t, 2 x int32
     assert ctypes.sizeof(gm._binding.Opts) == 32
-    assert ctypes.sizeof(gm._binding.Plan) == 48
+    assert ctypes.sizeof(gm._binding.Plan) == 56

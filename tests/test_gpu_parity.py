@@ -187,7 +187,16 @@ def test_prefetch_depth_does_not_change_results(orc, dtype):
     ref = orc.gemm64(A, B, dtype, "identity")
     for cid in _configs_of(dtype):
         outs = {}
+        sk_outs = {}
         for p in range(0, 5):
+            try:
+                sk = gm.get_plan(M, N, K, L, gm.DTYPE_CODES[dtype], gm.EPI_IDENTITY,
+                                 gm.make_opts(config_id=cid, prefetch_stages=p, streamk=True))
+            except gm.GemmMklError:
+                sk = None
+            if sk is not None:
+                assert sk["streamk"] == 1
+                sk_outs[p] = run_gemm(A, B, dtype, "identity", config_id=cid, prefetch_stages=p, streamk=True)
             try:
                 gm.get_plan(M, N, K, L, gm.DTYPE_CODES[dtype], gm.EPI_IDENTITY,
                             gm.make_opts(config_id=cid, prefetch_stages=p, split_k=1))
@@ -199,6 +208,11 @@ def test_prefetch_depth_does_not_change_results(orc, dtype):
         assert_close(first, ref, A, B, dtype, K, f"config {cid}")
         for p, C in outs.items():
             assert_bits_equal(C, first, f"config {cid} prefetch {p}")
+        if sk_outs:
+            sk_first = next(iter(sk_outs.values()))
+            assert_close(sk_first, ref, A, B, dtype, K, f"config {cid} stream-K")
+            for p, C in sk_outs.items():
+                assert_bits_equal(C, sk_first, f"config {cid} stream-K prefetch {p}")
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -308,3 +322,59 @@ def test_raw_c_abi_entry_point(orc):
     assert st == 0, gm.status_string(st)
     torch.cuda.synchronize()
     assert_close(workloads.torch_to_storage(c), orc.gemm64(A, B, "f16", "silu"), A, B, "f16", K, "raw ABI")
+
+
+# ---------------------------------------------------------------- stream-K
+
+SK_SHAPES = [(300, 390, 1552, 2), (512, 640, 2048, 1), (129, 257, 1000, 3), (64, 64, 4096, 1)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape", SK_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_streamk_parity_and_determinism(orc, dtype, shape):
+    """Stream-K (forced): oracle parity, integer inputs bit-exact, and the same
+    bits on every run (the fix-up sums pieces in a fixed order)."""
+    M, N, K, L = shape
+    code = gm.DTYPE_CODES[dtype]
+    try:
+        plan = gm.get_plan(M, N, K, L, code, gm.EPI_SILU, gm.make_opts(streamk=True))
+    except gm.GemmMklError as e:
+        assert e.status == -6
+        pytest.skip("no stream-K configuration fits this shape")
+    assert plan["streamk"] == 1 and plan["grid"] <= 256
+    A, B = _operands(dtype, M, N, K, L, seed=K + 7)
+    ref = orc.gemm64(A, B, dtype, "silu")
+    C1 = run_gemm(A, B, dtype, "silu", streamk=True)
+    assert_close(C1, ref, A, B, dtype, K, f"stream-K {dtype} {shape}")
+    C2 = run_gemm(A, B, dtype, "silu", streamk=True)
+    assert_bits_equal(C1, C2, "stream-K run-to-run")
+    Ai, Bi = _operands(dtype, M, N, K, L, seed=K + 8, integer=True)
+    refi = orc.round_to_dtype(orc.gemm64(Ai, Bi, dtype, "relu"), dtype)
+    assert_bits_equal(run_gemm(Ai, Bi, dtype, "relu", streamk=True), refi, f"stream-K integer {dtype} {shape}")
+
+
+def test_streamk_caller_workspace_counters_return_to_zero(orc):
+    import torch
+
+    M, N, K, L = 512, 640, 2048, 1
+    A, B = _operands("bf16", M, N, K, L, seed=31)
+    a, b = to_device(A, "bf16"), to_device(B, "bf16")
+    plan = gm.get_plan(M, N, K, L, gm.BF16, gm.EPI_RELU, gm.make_opts(streamk=True))
+    assert plan["streamk"] == 1 and plan["counter_bytes"] > 0
+    ws = torch.zeros(plan["workspace_bytes"] // 4 + 1024, dtype=torch.float32, device=a.device)
+    outs = []
+    for _ in range(3):
+        outs.append(gm.gemm(a, b, "relu", streamk=True, workspace=ws))
+        torch.cuda.synchronize()
+        assert torch.all(ws[: plan["counter_bytes"] // 4] == 0).item(), "counters left non-zero"
+    internal = gm.gemm(a, b, "relu", streamk=True)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert_bits_equal(workloads.torch_to_storage(o), workloads.torch_to_storage(internal), "caller ws")
+    assert_close(workloads.torch_to_storage(internal), orc.gemm64(A, B, "bf16", "relu"), A, B, "bf16", K, "sk")
+
+
+def test_streamk_and_split_k_exclude_each_other():
+    with pytest.raises(gm.GemmMklError) as e:
+        gm.get_plan(512, 640, 2048, 1, gm.BF16, gm.EPI_RELU, gm.make_opts(streamk=True, split_k=2))
+    assert e.value.status == -6

@@ -15,6 +15,7 @@ constexpr int kMaxPrefetch = 4;   // prefetch_stages 0..4 (ring of 1..5 LDS slot
 constexpr int kModes = 4;         // identity, relu, silu, split-K partial
 
 typedef hipError_t (*TileLaunchFn)(const TileParams &p, int grid, hipStream_t stream);
+typedef hipError_t (*StreamKLaunchFn)(const StreamKParams &p, int grid, hipStream_t stream);
 typedef hipError_t (*ReduceLaunchFn)(const float *W, void *C, int64_t total, int split, hipStream_t stream);
 typedef hipError_t (*GeneralLaunchFn)(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
                                       int64_t L, hipStream_t stream);
@@ -26,8 +27,10 @@ struct ConfigEntry {
     int mf;                // MFMA block edge (16 or 32)
     int waves_m, waves_n;  // wave grid (64 lanes each)
     int default_p;         // prefetch_stages used when not forced
+    float eff;             // measured fraction of the dtype's MFMA peak on large problems
     const char *name;
     TileLaunchFn fn[kMaxPrefetch + 1][kModes];  // null where not instantiated
+    StreamKLaunchFn sk[kMaxPrefetch + 1][3];    // stream-K by epilogue, null where not instantiated
 };
 
 struct DtypeKernels {
@@ -50,6 +53,23 @@ hipError_t launch_tile(const TileParams &p, int grid, hipStream_t stream)
     return hipGetLastError();
 }
 
+template <class T, int BM, int BN, int RB, int WMW, int WNW, int MF, int P, int MODE>
+hipError_t launch_streamk(const StreamKParams &p, int grid, hipStream_t stream)
+{
+    hipLaunchKernelGGL((gemm_streamk_kernel<T, BM, BN, RB, WMW, WNW, MF, P, MODE>), dim3(grid),
+                       dim3(WMW * WNW * 64), 0, stream, p);
+    return hipGetLastError();
+}
+
+// Stream-K variants of a configuration for prefetch depth P.
+template <class T, int BM, int BN, int RB, int WMW, int WNW, int MF, int P>
+void fill_streamk(ConfigEntry &e)
+{
+    e.sk[P][MODE_IDENTITY] = &launch_streamk<T, BM, BN, RB, WMW, WNW, MF, P, MODE_IDENTITY>;
+    e.sk[P][MODE_RELU] = &launch_streamk<T, BM, BN, RB, WMW, WNW, MF, P, MODE_RELU>;
+    e.sk[P][MODE_SILU] = &launch_streamk<T, BM, BN, RB, WMW, WNW, MF, P, MODE_SILU>;
+}
+
 template <class T, int BM, int BN, int RB, int WMW, int WNW, int MF, int P>
 void fill_prefetch(ConfigEntry &e)
 {
@@ -62,9 +82,10 @@ void fill_prefetch(ConfigEntry &e)
 // A configuration: tile BM x BN, RB bytes of K per row and chunk, a WMW x WNW
 // wave grid, MFMA edge MF, instantiated for prefetch depths Ps.
 template <class T, int BM, int BN, int RB, int WMW, int WNW, int MF, int... Ps>
-ConfigEntry make_entry(int dtype, int default_p, const char *name)
+ConfigEntry make_entry(int dtype, int default_p, float eff, const char *name)
 {
     ConfigEntry e{};
+    e.eff = eff;
     e.dtype = dtype;
     e.bm = BM;
     e.bn = BN;
@@ -75,6 +96,14 @@ ConfigEntry make_entry(int dtype, int default_p, const char *name)
     e.default_p = default_p;
     e.name = name;
     (fill_prefetch<T, BM, BN, RB, WMW, WNW, MF, Ps>(e), ...);
+    return e;
+}
+
+// Adds stream-K variants (prefetch depths Ps) to an entry made by make_entry.
+template <class T, int BM, int BN, int RB, int WMW, int WNW, int MF, int... Ps>
+ConfigEntry with_streamk(ConfigEntry e)
+{
+    (fill_streamk<T, BM, BN, RB, WMW, WNW, MF, Ps>(e), ...);
     return e;
 }
 

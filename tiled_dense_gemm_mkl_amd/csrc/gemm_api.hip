@@ -71,6 +71,9 @@ struct Plan {
     int P = 0;
     int S = 1;
     bool general = false;
+    bool streamk = false;
+    int64_t sk_units = 0;          // stream-K: tiles (all batches) * chunks per tile
+    size_t sk_counter_bytes = 0;   // stream-K: per-tile counters, 256-byte padded
     int64_t grid = 0;
     int32_t tiles_m = 0, tiles_n = 0, group_m = 1;
     int32_t total_chunks = 0, chunks_per_split = 0;
@@ -95,7 +98,10 @@ int check_args(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, int epilog
         if (o->prefetch_stages < -1) return GEMM_MKL_STATUS_INVALID_VALUE;
         if (o->split_k < 0) return GEMM_MKL_STATUS_INVALID_VALUE;
         if (o->config_id < -1) return GEMM_MKL_STATUS_INVALID_VALUE;
-        if (o->flags & ~(int32_t)GEMM_MKL_OPT_FORCE_GENERAL) return GEMM_MKL_STATUS_INVALID_VALUE;
+        const int32_t known = GEMM_MKL_OPT_FORCE_GENERAL | GEMM_MKL_OPT_STREAMK | GEMM_MKL_OPT_NO_STREAMK;
+        if (o->flags & ~known) return GEMM_MKL_STATUS_INVALID_VALUE;
+        if ((o->flags & GEMM_MKL_OPT_STREAMK) && (o->flags & GEMM_MKL_OPT_NO_STREAMK))
+            return GEMM_MKL_STATUS_INVALID_VALUE;
         if (o->workspace == nullptr && o->workspace_bytes != 0) return GEMM_MKL_STATUS_INVALID_VALUE;
         if (o->workspace && (reinterpret_cast<uintptr_t>(o->workspace) & 255)) return GEMM_MKL_STATUS_INVALID_VALUE;
     }
@@ -112,14 +118,7 @@ double model_cycles(const ConfigEntry &c, int dtype, int64_t M, int64_t N, int64
     const int chunks = (total_chunks + S - 1) / S;
     const double bk = (double)c.rb / elem_bytes(dtype);
     const double peak = dtype == GEMM_MKL_F32 ? 256.0 : 4096.0;  // flop / clk / CU
-    double eff;
-    const int area = c.bm * c.bn;
-    if (dtype == GEMM_MKL_F32)
-        eff = area >= 128 * 128 ? 0.8 : (area >= 64 * 64 ? 0.7 : 0.5);
-    else if (c.mf == 16)
-        eff = 0.3;
-    else
-        eff = area >= 256 * 256 ? 0.85 : (area >= 256 * 128 ? 0.75 : (area >= 128 * 128 ? 0.6 : 0.3));
+    const double eff = c.eff;
     const double per_chunk = 2.0 * c.bm * c.bn * bk / (peak * eff) + 60.0;
     double cyc = (double)rounds * (chunks * per_chunk + 1500.0);
     if (S > 1) {
@@ -141,6 +140,43 @@ bool fast_path_ok(const ConfigEntry &c, int dtype, int64_t K)
     return true;
 }
 
+// Largest number of ranges (pieces) one tile's chunks fall into when U units
+// are cut into G ranges of floor/ceil(U/G) units.
+int64_t max_pieces(int64_t U, int64_t G, int64_t C)
+{
+    const int64_t minr = U / G;
+    if (minr < 1) return INT64_MAX;
+    return (C + minr - 1) / minr + 1;
+}
+
+constexpr int kMaxPieces = 8;   // pieces per tile the stream-K kernel can combine
+
+// Stream-K grid: one workgroup per CU, fewer when needed so that every range
+// holds at least ceil(C / (kMaxPieces - 1)) units (at most kMaxPieces pieces per tile).
+int64_t streamk_grid(int64_t U, int64_t C)
+{
+    const int64_t need = (C + kMaxPieces - 2) / (kMaxPieces - 1);
+    int64_t G = std::min<int64_t>(kNumCUs, U / std::max<int64_t>(need, 1));
+    return std::max<int64_t>(G, 1);
+}
+
+// Modelled stream-K time: every CU runs ceil(U / G) chunks, plus the fix-up of
+// split tiles (save and read back an fp32 tile, fences, counters).
+double model_streamk_cycles(const ConfigEntry &c, int dtype, int64_t M, int64_t N, int64_t K, int64_t L)
+{
+    const int64_t C = (K * elem_bytes(dtype) + c.rb - 1) / c.rb;
+    const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn) * L;
+    const int64_t U = tiles * C;
+    const int64_t G = streamk_grid(U, C);
+    const double one_round = model_cycles(c, dtype, M, N, K, L, 1);
+    const int64_t rounds = (tiles + kNumCUs - 1) / kNumCUs;
+    const double per_chunk = (one_round / (double)rounds - 1500.0) / (double)C;
+    const int64_t per_wg = (U + G - 1) / G;
+    double cyc = per_wg * per_chunk + 1500.0;
+    if (U % G != 0 || per_wg % C != 0) cyc += 2.0 * c.bm * c.bn * 4.0 / 64.0 + 2000.0;
+    return cyc;
+}
+
 int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_mkl_opts *o, bool ptrs_aligned,
               Plan *plan)
 {
@@ -153,6 +189,15 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
     int forced_s = o ? o->split_k : 0;
     if (forced_s <= 0) forced_s = env_int("GEMM_MKL_SPLIT_K", 0);
     const bool force_general = o && (o->flags & GEMM_MKL_OPT_FORCE_GENERAL);
+    // stream-K: -1 automatic, 0 never, 1 always (where a configuration has it)
+    // (automatic choice is off until the stream-K fix-up beats the data-parallel grid)
+    int sk_mode = env_int("GEMM_MKL_STREAMK", 0);
+    if (o && (o->flags & GEMM_MKL_OPT_STREAMK)) sk_mode = 1;
+    if (o && (o->flags & GEMM_MKL_OPT_NO_STREAMK)) sk_mode = 0;
+    // an explicit split_k selects the split-K grid (1: no split of K at all);
+    // stream-K then only runs when forced, and never together with a split
+    if (forced_s > 1 && sk_mode == 1) return GEMM_MKL_STATUS_NOT_AVAILABLE;
+    if (forced_s >= 1 && sk_mode != 1) sk_mode = 0;
 
     if (forced_cfg >= (int)R.table.size()) return GEMM_MKL_STATUS_NOT_AVAILABLE;
     if (forced_cfg >= 0 && R.table[forced_cfg].dtype != dtype) return GEMM_MKL_STATUS_NOT_AVAILABLE;
@@ -173,7 +218,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
         }
     }
     if (general) {
-        if (forced_cfg >= 0 || forced_p >= 0 || forced_s > 1) return GEMM_MKL_STATUS_NOT_AVAILABLE;
+        if (forced_cfg >= 0 || forced_p >= 0 || forced_s > 1 || sk_mode == 1) return GEMM_MKL_STATUS_NOT_AVAILABLE;
         plan->general = true;
         plan->config_id = -1;
         plan->P = 0;
@@ -186,17 +231,33 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
         return GEMM_MKL_STATUS_OK;
     }
 
-    // candidate (config, split) pairs
+    // candidate (config, split) pairs and stream-K configurations
     double best = 1e300;
     int best_c = -1, best_s = 1;
+    bool best_sk = false;
     for (int id = 0; id < (int)R.table.size(); ++id) {
         const ConfigEntry &c = R.table[id];
         if (c.dtype != dtype) continue;
         if (forced_cfg >= 0 && id != forced_cfg) continue;
         if (!fast_path_ok(c, dtype, K)) continue;
         const int p = forced_p >= 0 ? forced_p : c.default_p;
-        if (c.fn[p][0] == nullptr) continue;
         const int total_chunks = (int)((K * es + c.rb - 1) / c.rb);
+        if (sk_mode != 0 && c.sk[p][0] != nullptr && total_chunks > 0) {
+            const int64_t tiles_all = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn) * L;
+            const int64_t U = tiles_all * total_chunks;
+            const int64_t G = streamk_grid(U, total_chunks);
+            if (max_pieces(U, G, total_chunks) <= kMaxPieces && tiles_all <= INT32_MAX) {
+                const double cyc = model_streamk_cycles(c, dtype, M, N, K, L);
+                if (cyc < best) {
+                    best = cyc;
+                    best_c = id;
+                    best_s = 1;
+                    best_sk = true;
+                }
+            }
+        }
+        if (sk_mode == 1) continue;
+        if (c.fn[p][0] == nullptr) continue;
         for (int S = 1; S <= kMaxSplit; ++S) {
             if (forced_s > 0 && S != forced_s) continue;
             if (forced_s <= 0 && S > 1 && (total_chunks + S - 1) / S < 4) break;
@@ -207,6 +268,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
                 best = cyc;
                 best_c = id;
                 best_s = S;
+                best_sk = false;
             }
         }
     }
@@ -235,18 +297,70 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
     plan->grid = (int64_t)plan->tiles_m * plan->tiles_n * plan->S * L;
     if (plan->grid > INT32_MAX) return GEMM_MKL_STATUS_NOT_AVAILABLE;
     plan->ws_bytes = plan->S > 1 ? (size_t)plan->S * (size_t)(L * M * N) * 4 : 0;
+    plan->streamk = best_sk;
+    if (best_sk) {
+        const int64_t tiles_all = (int64_t)plan->tiles_m * plan->tiles_n * L;
+        plan->sk_units = tiles_all * total_chunks;
+        plan->grid = streamk_grid(plan->sk_units, total_chunks);
+        plan->sk_counter_bytes = ((size_t)tiles_all * 4 + 255) / 256 * 256;
+        // [counters][2 partial tiles per workgroup]
+        plan->ws_bytes = plan->sk_counter_bytes + (size_t)2 * plan->grid * c.bm * c.bn * 4;
+    }
     return GEMM_MKL_STATUS_OK;
 }
 
 // ---------------------------------------------------------------- internal workspace
 
 struct Workspace {
-    void *ptr = nullptr;
+    void *ptr = nullptr;        // split-K / stream-K partial sums
     size_t bytes = 0;
+    void *counters = nullptr;   // stream-K per-tile counters: zero between calls
+    size_t counter_bytes = 0;
 };
 
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+// Per-tile stream-K counters of (device, stream): zeroed when allocated, and
+// every completed stream-K call leaves them zero again.
+int get_counters(hipStream_t stream, size_t need, void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        t_last_hip = e;
+        return GEMM_MKL_STATUS_HIP_ERROR;
+    }
+    std::lock_guard<std::mutex> g(g_ws_mutex);
+    Workspace &w = g_ws[std::make_pair(dev, stream)];
+    if (w.counter_bytes < need) {
+        if (w.counters) {
+            e = hipStreamSynchronize(stream);
+            if (e == hipSuccess) e = hipFree(w.counters);
+            w.counters = nullptr;
+            w.counter_bytes = 0;
+            if (e != hipSuccess) {
+                t_last_hip = e;
+                return GEMM_MKL_STATUS_HIP_ERROR;
+            }
+        }
+        size_t sz = need < (size_t)65536 ? (size_t)65536 : need;
+        e = hipMalloc(&w.counters, sz);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            w.counters = nullptr;
+            return GEMM_MKL_STATUS_WORKSPACE;
+        }
+        e = hipMemsetAsync(w.counters, 0, sz, stream);
+        if (e != hipSuccess) {
+            t_last_hip = e;
+            return GEMM_MKL_STATUS_HIP_ERROR;
+        }
+        w.counter_bytes = sz;
+    }
+    *out = w.counters;
+    return GEMM_MKL_STATUS_OK;
+}
 
 int get_workspace(hipStream_t stream, size_t need, void **out)
 {
@@ -305,10 +419,10 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
     Registry &R = registry();
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
     if (env_int("GEMM_MKL_LOG", 0))
-        std::fprintf(stderr, "gemm_mkl: M=%lld N=%lld K=%lld L=%lld dtype=%d epi=%d -> %s P=%d S=%d grid=%lld\n",
+        std::fprintf(stderr, "gemm_mkl: M=%lld N=%lld K=%lld L=%lld dtype=%d epi=%d -> %s P=%d S=%d%s grid=%lld\n",
                      (long long)M, (long long)N, (long long)K, (long long)L, dtype, epilogue,
                      plan.general ? "general" : R.table[plan.config_id].name, plan.P, plan.S,
-                     (long long)plan.grid);
+                     plan.streamk ? " stream-K" : "", (long long)plan.grid);
 
     hipError_t e;
     if (plan.general) {
@@ -328,7 +442,26 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
         p.split = plan.S;
         p.chunks_per_split = plan.chunks_per_split;
         p.total_chunks = plan.total_chunks;
-        if (plan.S == 1) {
+        if (plan.streamk) {
+            p.C = C;
+            void *ws = nullptr, *cnt = nullptr;
+            if (o && o->workspace) {
+                if (o->workspace_bytes < plan.ws_bytes) return GEMM_MKL_STATUS_WORKSPACE;
+                cnt = o->workspace;
+                ws = static_cast<char *>(o->workspace) + plan.sk_counter_bytes;
+            } else {
+                st = get_workspace(stream, plan.ws_bytes - plan.sk_counter_bytes, &ws);
+                if (st != GEMM_MKL_STATUS_OK) return st;
+                st = get_counters(stream, plan.sk_counter_bytes, &cnt);
+                if (st != GEMM_MKL_STATUS_OK) return st;
+            }
+            StreamKParams sp;
+            sp.t = p;
+            sp.ws = reinterpret_cast<float *>(ws);
+            sp.counters = reinterpret_cast<int *>(cnt);
+            sp.units = plan.sk_units;
+            e = c.sk[plan.P][epilogue](sp, (int)plan.grid, stream);
+        } else if (plan.S == 1) {
             p.C = C;
             e = c.fn[plan.P][epilogue](p, (int)plan.grid, stream);
         } else {
@@ -411,6 +544,8 @@ int gemm_mkl_get_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, int
         out->threads = c.waves_m * c.waves_n * 64;
     }
     out->workspace_bytes = plan.ws_bytes;
+    out->streamk = plan.streamk ? 1 : 0;
+    out->counter_bytes = (int32_t)plan.sk_counter_bytes;
     return GEMM_MKL_STATUS_OK;
 }
 
@@ -431,9 +566,10 @@ int gemm_mkl_release_workspace(void)
     int cur = 0;
     (void)hipGetDevice(&cur);
     for (auto &kv : g_ws) {
-        if (kv.second.ptr) {
+        for (void *ptr : {kv.second.ptr, kv.second.counters}) {
+            if (!ptr) continue;
             hipError_t e = hipSetDevice(kv.first.first);
-            if (e == hipSuccess) e = hipFree(kv.second.ptr);
+            if (e == hipSuccess) e = hipFree(ptr);
             if (e != hipSuccess) {
                 t_last_hip = e;
                 st = GEMM_MKL_STATUS_HIP_ERROR;

@@ -251,6 +251,16 @@ __device__ __forceinline__ int row_swizzle(int r)
         return (r >> 2) & 3;
 }
 
+// Cache policy of the stream-K partial tiles: SC0 | SC1 (system scope), so the
+// stores write through to memory and the loads do not hit a stale line in
+// another XCD's L2; no L2-wide write-back or invalidate is needed.
+constexpr int kCoherent = 1 | 16;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(const float *base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+
 template <class T, int MF> struct Mfma;
 
 template <class T> struct Mfma<T, 16> {
@@ -284,116 +294,155 @@ template <class T> struct Mfma<T, 32> {
     }
 };
 
-// One workgroup computes a BM x BN tile of C (or of a split-K partial).
+// The work of one workgroup on one BM x BN tile of C: buffer descriptors and
+// per-lane load offsets for the tile, the prefetch ring over a range of K
+// chunks into fp32 accumulators, and the stores of the result.
 //   RB      bytes of K per row in one chunk (the K-outer step)
 //   MF      MFMA block edge: 32 (v_mfma_f32_32x32x16 / 32x32x2f32) or 16
 //   P       prefetch_stages: chunks in flight ahead of the one consumed
-//   MODE    epilogue (identity / ReLU / SiLU) or split-K partial store
-template <class T, int BM, int BN, int RB, int WAVES_M, int WAVES_N, int MF, int P, int MODE>
-__global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_tile_kernel(TileParams p)
-{
+template <class T, int BM, int BN, int RB, int WAVES_M, int WAVES_N, int MF, int P>
+struct TileCore {
     typedef Mfma<T, MF> MM;
     typedef typename MM::acc_t acc_t;
-    constexpr int NW = WAVES_M * WAVES_N;
-    constexpr int ES = Elem<T>::bytes;
-    constexpr int NCH = RB / 16;                  // 16-byte columns per row
-    constexpr int ROWS_PER_LOAD = 1024 / RB;      // rows covered by one 64-lane 16-byte load
-    constexpr int WTM = BM / WAVES_M;
-    constexpr int WTN = BN / WAVES_N;
-    constexpr int FM = WTM / MF;
-    constexpr int FN = WTN / MF;
-    constexpr int STEP_COLS = 64 / MF;            // 16-byte columns one MFMA k-step reads per row
-    constexpr int KSTEPS = NCH / STEP_COLS;
-    constexpr int LANE_ROWS = MF;                 // rows covered by one operand read (lanes mod MF)
-    constexpr int SLOTS = P + 1;
-    constexpr int SLOT_BYTES = (BM + BN) * RB;
-    constexpr int A_GROUPS = BM / ROWS_PER_LOAD;
-    constexpr int B_GROUPS = BN / ROWS_PER_LOAD;
-    constexpr int A_LOADS = A_GROUPS / NW;
-    constexpr int B_LOADS = B_GROUPS / NW;
-    constexpr int LOADS = A_LOADS + B_LOADS;
+    static constexpr int NW = WAVES_M * WAVES_N;
+    static constexpr int THREADS = NW * 64;
+    static constexpr int ES = Elem<T>::bytes;
+    static constexpr int NCH = RB / 16;                  // 16-byte columns per row
+    static constexpr int ROWS_PER_LOAD = 1024 / RB;      // rows covered by one 64-lane 16-byte load
+    static constexpr int WTM = BM / WAVES_M;
+    static constexpr int WTN = BN / WAVES_N;
+    static constexpr int FM = WTM / MF;
+    static constexpr int FN = WTN / MF;
+    static constexpr int STEP_COLS = 64 / MF;            // 16-byte columns one MFMA k-step reads per row
+    static constexpr int KSTEPS = NCH / STEP_COLS;
+    static constexpr int SLOTS = P + 1;
+    static constexpr int SLOT_BYTES = (BM + BN) * RB;
+    static constexpr int LDS_BYTES = SLOTS * SLOT_BYTES;
+    static constexpr int A_GROUPS = BM / ROWS_PER_LOAD;
+    static constexpr int B_GROUPS = BN / ROWS_PER_LOAD;
+    static constexpr int A_LOADS = A_GROUPS / NW;
+    static constexpr int B_LOADS = B_GROUPS / NW;
+    static constexpr int LOADS = A_LOADS + B_LOADS;
+    static constexpr int NMF = FM * FN;                  // MFMAs per k-step
+    static constexpr int NRD = FM + FN;                  // fragment reads per k-step
+    static constexpr int NREG = FM * FN * MM::regs;      // accumulator floats per lane
+    // Fragment reads run RA k-steps ahead of their MFMAs, in a ring of NB = RA + 1
+    // register buffers: one k-step of MFMAs covers the LDS latency when it holds
+    // at least 8 MFMAs; smaller wave tiles read KSTEPS - 1 steps ahead.
+    static constexpr int RA = (NMF >= 8 || KSTEPS < 4) ? 1 : KSTEPS - 1;
+    static constexpr int NB = RA + 1;
+    static_assert(KSTEPS % NB == 0, "fragment ring must divide the k-steps of a chunk");
+    // Chunk i + 1 is waited for at k-step WIN of chunk i.  The loads of chunk
+    // i + P are spread over the first SPREAD k-steps of chunk i: all of them
+    // (P >= 2, the wait then allows for the QW of them issued before k-step WIN)
+    // or, with P = 1 where chunk i + P is the one waited for, only those before
+    // the wait.
+    static constexpr int WIN = KSTEPS - RA;
+    static constexpr int SPREAD = P >= 2 ? KSTEPS : WIN;
+    static constexpr int LPK = (LOADS + SPREAD - 1) / SPREAD;      // loads per k-step
+    static constexpr int QW = (WIN * LPK < LOADS) ? WIN * LPK : LOADS;
+    static constexpr int WAIT_CNT = P >= 2 ? LOADS * (P - 2) + QW : 0;
     static_assert(RB == 64 || RB == 128, "row bytes");
     static_assert(MF == 16 || MF == 32, "MFMA shape");
     static_assert(BM % (MF * WAVES_M) == 0 && BN % (MF * WAVES_N) == 0, "wave tile");
     static_assert(A_GROUPS % NW == 0 && B_GROUPS % NW == 0, "load split");
     static_assert(KSTEPS >= 2 && KSTEPS % 2 == 0, "k-steps per chunk: even, for the register double buffer");
-    static_assert(SLOTS * SLOT_BYTES <= 160 * 1024, "LDS budget of a gfx950 workgroup");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 workgroup");
     static_assert(LOADS * (P > 0 ? P : 1) < 64, "vmcnt range");
+    static_assert(P < 2 || WAIT_CNT < LOADS * (P - 1) + 1, "wait count");
 
-    __shared__ __attribute__((aligned(1024))) char smem[SLOTS * SLOT_BYTES];
-
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-
-    // ---- tile mapping: [l][s][tile], tiles rastered in groups of group_m tile
-    // rows (column-major inside a group), after the XCD remap
-    int t = xcd_remap(blockIdx.x, gridDim.x);
-    const int tiles = p.tiles_m * p.tiles_n;
-    const int tile = t % tiles;
-    t /= tiles;
-    const int s = t % p.split;
-    const int l = t / p.split;
-    const int width = p.group_m * p.tiles_n;
-    const int first_m = (tile / width) * p.group_m;
-    const int gsize = min(p.tiles_m - first_m, p.group_m);
-    const int tm = first_m + (tile % width) % gsize;
-    const int tn = (tile % width) / gsize;
-
-    const int64_t m0 = (int64_t)tm * BM;
-    const int64_t n0 = (int64_t)tn * BN;
-    const int64_t K = p.K;
-    const int chunk0 = s * p.chunks_per_split;
-    int nk = p.total_chunks - chunk0;
-    if (nk > p.chunks_per_split) nk = p.chunks_per_split;
-    if (nk < 0) nk = 0;
-
-    // ---- buffer resources anchored at the tile's first row
-    const T *Ab = reinterpret_cast<const T *>(p.A) + ((int64_t)l * p.M + m0) * K;
-    const T *Bb = reinterpret_cast<const T *>(p.B) + ((int64_t)l * p.N + n0) * K;
-    const int64_t rows_a = p.M - m0;
-    const int64_t rows_b = p.N - n0;
-    const int64_t bytes_a = rows_a * K * ES;
-    const int64_t bytes_b = rows_b * K * ES;
-    // the descriptors start kRsrcBias bytes early (see dma16_same_m0); nothing
-    // is ever read there, and the range check still ends at the tile's last row
-    const int64_t lim_a = bytes_a + kRsrcBias, lim_b = bytes_b + kRsrcBias;
-    const i32x4 rsrc_a = make_rsrc(reinterpret_cast<const char *>(Ab) - kRsrcBias,
-                                   (uint32_t)(lim_a < (int64_t)kOutOfRange ? lim_a : kOutOfRange));
-    const i32x4 rsrc_b = make_rsrc(reinterpret_cast<const char *>(Bb) - kRsrcBias,
-                                   (uint32_t)(lim_b < (int64_t)kOutOfRange ? lim_b : kOutOfRange));
-
-    // ---- per-lane load offsets.  Wave w loads the row groups
-    // [w * A_LOADS, (w + 1) * A_LOADS) of A (and likewise of B), so that its
-    // blocks are contiguous in LDS; lane -> (row lane / NCH of the group,
-    // physical column lane % NCH, holding logical column that ^ swizzle(row)).
+    char *smem;
+    uint32_t smem_base;
+    int lane, wave, wm, wn, lrow, lcol, sw;
+    uint32_t rd_a, rd_b;
+    int64_t m0, n0, k_bytes;
+    int l;
+    i32x4 rsrc_a, rsrc_b;
     uint32_t voff_a[A_LOADS], voff_b[B_LOADS];
     int col_a[A_LOADS], col_b[B_LOADS];
-    const int64_t row_bytes_g = K * ES;
-#pragma unroll
-    for (int j = 0; j < A_LOADS; ++j) {
-        const int g = wave * A_LOADS + j;
-        const int r = g * ROWS_PER_LOAD + lane / NCH;
-        const int c = (lane % NCH) ^ row_swizzle<RB>(r);
-        col_a[j] = c;
-        voff_a[j] = (r < rows_a) ? (uint32_t)(r * row_bytes_g + c * 16 + kRsrcBias - (j & 3) * 1024) : kOutOfRange;
-    }
-#pragma unroll
-    for (int j = 0; j < B_LOADS; ++j) {
-        const int g = wave * B_LOADS + j;
-        const int r = g * ROWS_PER_LOAD + lane / NCH;
-        const int c = (lane % NCH) ^ row_swizzle<RB>(r);
-        col_b[j] = c;
-        voff_b[j] = (r < rows_b) ? (uint32_t)(r * row_bytes_g + c * 16 + kRsrcBias - (j & 3) * 1024) : kOutOfRange;
-    }
-    const uint32_t smem_base = lds_addr(smem);
-    const int64_t k_bytes = K * ES;
+    acc_t acc[FM][FN];
+    i32x4 fa[NB][FM], fb[NB][FN];
 
-    // Load q (0 <= q < LOADS) of one chunk: q < A_LOADS are A row groups, the
-    // rest B row groups.  Every wave issues the same number of loads per chunk,
-    // which is what the vmcnt waits below count.
-    auto issue_one = [&](int chunk, int slot, int q) {
-        const int64_t kb = (int64_t)(chunk0 + chunk) * RB;   // byte offset of the chunk in a row
-        const int64_t rem = k_bytes - kb;                     // bytes of the row left from kb
+    __device__ __forceinline__ void init(char *lds)
+    {
+        smem = lds;
+        smem_base = lds_addr(lds);
+        lane = threadIdx.x & 63;
+        wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        wm = wave % WAVES_M;
+        wn = wave / WAVES_M;
+        // operand reads: lane reads row (lane % MF) of each fragment at logical
+        // column ks * STEP_COLS + lane / MF
+        lrow = lane % MF;
+        lcol = lane / MF;
+        sw = row_swizzle<RB>(lrow);
+        rd_a = (uint32_t)((wm * WTM + lrow) * RB);
+        rd_b = (uint32_t)(BM * RB + (wn * WTN + lrow) * RB);
+    }
+
+    // Buffer descriptors and per-lane offsets for tile (l, tm, tn).
+    __device__ __forceinline__ void setup(const TileParams &p, int l_, int tm, int tn)
+    {
+        l = l_;
+        m0 = (int64_t)tm * BM;
+        n0 = (int64_t)tn * BN;
+        const int64_t K = p.K;
+        k_bytes = K * ES;
+        const T *Ab = reinterpret_cast<const T *>(p.A) + ((int64_t)l * p.M + m0) * K;
+        const T *Bb = reinterpret_cast<const T *>(p.B) + ((int64_t)l * p.N + n0) * K;
+        const int64_t rows_a = p.M - m0;
+        const int64_t rows_b = p.N - n0;
+        // the descriptors start kRsrcBias bytes early (see dma16_same_m0);
+        // nothing is ever read there, and the range check still ends at the
+        // tile's last row
+        const int64_t lim_a = rows_a * k_bytes + kRsrcBias, lim_b = rows_b * k_bytes + kRsrcBias;
+        rsrc_a = make_rsrc(reinterpret_cast<const char *>(Ab) - kRsrcBias,
+                           (uint32_t)(lim_a < (int64_t)kOutOfRange ? lim_a : kOutOfRange));
+        rsrc_b = make_rsrc(reinterpret_cast<const char *>(Bb) - kRsrcBias,
+                           (uint32_t)(lim_b < (int64_t)kOutOfRange ? lim_b : kOutOfRange));
+        // Wave w loads the row groups [w * A_LOADS, (w + 1) * A_LOADS) of A
+        // (and likewise of B), so that its blocks are contiguous in LDS;
+        // lane -> (row lane / NCH of the group, physical column lane % NCH,
+        // holding logical column that ^ swizzle(row)).
+#pragma unroll
+        for (int j = 0; j < A_LOADS; ++j) {
+            const int g = wave * A_LOADS + j;
+            const int r = g * ROWS_PER_LOAD + lane / NCH;
+            const int c = (lane % NCH) ^ row_swizzle<RB>(r);
+            col_a[j] = c;
+            voff_a[j] = (r < rows_a) ? (uint32_t)(r * k_bytes + c * 16 + kRsrcBias - (j & 3) * 1024) : kOutOfRange;
+        }
+#pragma unroll
+        for (int j = 0; j < B_LOADS; ++j) {
+            const int g = wave * B_LOADS + j;
+            const int r = g * ROWS_PER_LOAD + lane / NCH;
+            const int c = (lane % NCH) ^ row_swizzle<RB>(r);
+            col_b[j] = c;
+            voff_b[j] = (r < rows_b) ? (uint32_t)(r * k_bytes + c * 16 + kRsrcBias - (j & 3) * 1024) : kOutOfRange;
+        }
+    }
+
+    __device__ __forceinline__ void zero()
+    {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int q = 0; q < MM::regs; ++q)
+                    acc[i][j][q] = 0.0f;
+    }
+
+    // Load q (0 <= q < LOADS) of chunk `chunk` (absolute index along K) into
+    // `slot`: q < A_LOADS are A row groups, the rest B row groups.  Every wave
+    // issues the same number of loads per chunk, which is what the vmcnt waits
+    // count.
+    // A load with valid == false reads nothing from memory and fills its LDS
+    // block with zeros (it keeps the per-chunk load count uniform).
+    __device__ __forceinline__ void issue_one(int chunk, int slot, int q, bool valid = true)
+    {
+        const int64_t kb = (int64_t)chunk * RB;   // byte offset of the chunk in a row
+        const int64_t rem = valid ? k_bytes - kb : 0;   // bytes of the row left from kb
         const uint32_t soff = (uint32_t)kb;
         const uint32_t sbase = smem_base + slot * SLOT_BYTES;
         if (q < A_LOADS) {
@@ -411,186 +460,374 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_tile_kernel(TilePa
             else
                 dma16_same_m0(rsrc_b, j & 3, v, soff);
         }
-    };
-    auto issue = [&](int chunk, int slot) {
-#pragma unroll
-        for (int q = 0; q < LOADS; ++q) issue_one(chunk, slot, q);
-    };
+    }
 
-    // ---- operand reads: lane reads row (lane % MF) of each fragment at logical
-    // column ks * STEP_COLS + lane / MF
-    const int wm = wave % WAVES_M;
-    const int wn = wave / WAVES_M;
-    const int lrow = lane % LANE_ROWS;
-    const int lcol = lane / LANE_ROWS;
-    const int sw = row_swizzle<RB>(lrow);
-    const uint32_t rd_a = (uint32_t)((wm * WTM + lrow) * RB);
-    const uint32_t rd_b = (uint32_t)(BM * RB + (wn * WTN + lrow) * RB);
+    __device__ __forceinline__ void issue(int chunk, int slot, bool valid = true)
+    {
+#pragma unroll
+        for (int q = 0; q < LOADS; ++q) issue_one(chunk, slot, q, valid);
+    }
 
-    acc_t acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int q = 0; q < MM::regs; ++q)
-                acc[i][j][q] = 0.0f;
-
-    // operand fragments, double-buffered in registers: the reads for k-step
-    // ks + 1 are issued between the MFMAs of k-step ks
-    constexpr int NMF = FM * FN;                  // MFMAs per k-step
-    constexpr int NRD = FM + FN;                  // fragment reads per k-step
-    i32x4 fa[2][FM], fb[2][FN];
-    auto read_one = [&](int slot, int ks, int buf, int r) {
+    __device__ __forceinline__ void read_one(int slot, int ks, int buf, int r)
+    {
         const char *base = smem + slot * SLOT_BYTES;
         const int col = ((ks * STEP_COLS + lcol) ^ sw) * 16;
         if (r < FM)
             fa[buf][r] = *reinterpret_cast<const i32x4 *>(base + rd_a + r * MF * RB + col);
         else
             fb[buf][r - FM] = *reinterpret_cast<const i32x4 *>(base + rd_b + (r - FM) * MF * RB + col);
-    };
-    auto mfma_one = [&](int buf, int t) {
+    }
+
+    __device__ __forceinline__ void mfma_one(int buf, int t)
+    {
         const int i = t / FN, j = t % FN;
         acc[i][j] = MM::step(fb[buf][j], fa[buf][i], acc[i][j]);
-    };
+    }
 
-    if constexpr (P == 0) {
-        for (int i = 0; i < nk; ++i) {
-            lds_barrier();                 // everyone is done reading the single slot
-            issue(i, 0);
-            wait_vmcnt<0>();
-            lds_barrier();                 // every wave's part of chunk i has landed
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-#pragma unroll
-                for (int r = 0; r < NRD; ++r) read_one(0, ks, ks & 1, r);
-#pragma unroll
-                for (int t = 0; t < NMF; ++t) mfma_one(ks & 1, t);
-            }
-        }
-    } else {
-        // The ring.  During iteration i (consuming chunk i from slot i mod
-        // SLOTS) the loads of chunk i + P go to slot (i + P) mod SLOTS, the slot
-        // chunk i - 1 used, spread between the MFMAs.  At the end of iteration i
-        // chunk i + 1 is waited for, a barrier makes every wave's part of it
-        // visible and retires every wave's reads of chunk i, and the first
-        // fragments of chunk i + 1 are read under the last MFMAs of chunk i.
-        constexpr int LPK = (LOADS + KSTEPS - 1) / KSTEPS;        // loads per k-step
-        constexpr int LGAP = (NMF / LPK) > 0 ? (NMF / LPK) : 1;    // MFMAs between loads
-        constexpr int RGAP = 1;   // reads go right behind the first MFMAs, so they land well before use
-#pragma unroll
-        for (int c = 0; c < P; ++c)
-            if (c < nk) issue(c, c);
-        if (nk > 0) {
-            if (nk - 1 >= P - 1)
-                wait_vmcnt<LOADS * (P - 1)>();
-            else
+    // acc += sum over chunks [c_begin, c_begin + nk) of the tile.  On entry no
+    // load of this workgroup is in flight; on exit none is, and every wave is
+    // past its last LDS read of the range.
+    __device__ void run(int c_begin, int nk)
+    {
+        lds_barrier();   // the slots may still be read by a previous range
+        if constexpr (P == 0) {
+            for (int i = 0; i < nk; ++i) {
+                if (i > 0) lds_barrier();   // everyone is done reading the single slot
+                issue(c_begin + i, 0);
                 wait_vmcnt<0>();
+                lds_barrier();              // every wave's part of chunk i has landed
+#pragma unroll
+                for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+                    for (int r = 0; r < NRD; ++r) read_one(0, ks, ks & 1, r);
+#pragma unroll
+                    for (int t = 0; t < NMF; ++t) mfma_one(ks & 1, t);
+                }
+            }
+        } else if (nk > 0) {
+            // The ring.  During iteration i (consuming chunk i from slot i mod
+            // SLOTS) the loads of chunk i + P go to slot (i + P) mod SLOTS, the
+            // slot chunk i - 1 used, spread between the MFMAs of the first WIN
+            // k-steps.  At k-step WIN of chunk i, chunk i + 1 is waited for and
+            // a barrier makes every wave's part of it visible and retires every
+            // wave's reads of chunk i (all issued by then: reads run RA steps
+            // ahead); the fragments of chunk i + 1's first RA k-steps are then
+            // read under the last MFMAs of chunk i.
+            //
+            // The loop body has no branches, so that the compiler can count
+            // the LDS reads in flight exactly: past the last chunk the loads
+            // become zero fills of the free slot (valid == false) and the reads
+            // of the chunk after the last one land in registers that are never
+            // used.  Exactly P chunks of loads are always in flight after a
+            // chunk's wait, hence one vmcnt value for every wait.
+            constexpr int LGAP = (NMF / LPK) > 0 ? (NMF / LPK) : 1;    // MFMAs between loads
+#pragma unroll
+            for (int c = 0; c < P; ++c) issue(c_begin + min(c, nk - 1), c, c < nk);
+            wait_vmcnt<LOADS * (P - 1)>();
             lds_barrier();
 #pragma unroll
-            for (int r = 0; r < NRD; ++r) read_one(0, 0, 0, r);
-        }
-        int slot = 0;
-        int fill = P;                      // slot that receives chunk i + P
-        for (int i = 0; i < nk; ++i) {
-            const int next = (slot + 1 == SLOTS) ? 0 : slot + 1;
-            const bool do_issue = i + P < nk;
+            for (int ks = 0; ks < RA; ++ks)
 #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                const bool last = ks + 1 == KSTEPS;
-                if (last) {
-                    // remaining loads of chunk i + P, then chunk i + 1 must have
-                    // landed: chunks issued after it so far: min(P - 1, nk - 2 - i)
+                for (int r = 0; r < NRD; ++r) read_one(0, ks, ks % NB, r);
+            int slot = 0;
+            int fill = P;   // slot that receives chunk i + P
+            for (int i = 0; i < nk; ++i) {
+                const int next = (slot + 1 == SLOTS) ? 0 : slot + 1;
+                const bool valid = i + P < nk;
+                const int load_chunk = c_begin + min(i + P, nk - 1);
 #pragma unroll
-                    for (int q = ks * LPK; q < LOADS; ++q)
-                        if (do_issue) issue_one(i + P, fill, q);
-                    if (i + 1 < nk) {
-                        if (nk - 2 - i >= P - 1)
-                            wait_vmcnt<LOADS * (P - 1)>();
-                        else
-                            wait_vmcnt<0>();
+                for (int ks = 0; ks < KSTEPS; ++ks) {
+                    const int t = ks + RA;                 // k-step whose fragments are read now
+                    const bool in_next = t >= KSTEPS;      // ... of chunk i + 1
+                    const int tks = in_next ? t - KSTEPS : t;
+                    const int tbuf = t % NB;
+                    const int rslot = in_next ? next : slot;
+                    if (ks == WIN) {
+                        // chunk i + 1 has landed once at most the loads issued
+                        // after it are in flight: chunks i + 2 .. i + P - 1 and
+                        // the first QW loads of chunk i + P
+                        wait_vmcnt<WAIT_CNT>();
                         lds_barrier();
                     }
-                }
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int t = 0; t < NMF; ++t) {
-                    mfma_one(ks & 1, t);
-                    if (t % RGAP == 0 && t / RGAP < NRD) {
-                        if (!last)
-                            read_one(slot, ks + 1, (ks + 1) & 1, t / RGAP);
-                        else if (i + 1 < nk)
-                            read_one(next, 0, 0, t / RGAP);
-                    }
-                    if (!last && t % LGAP == 0 && t / LGAP < LPK) {
-                        const int q = ks * LPK + t / LGAP;
-                        if (q < LOADS && do_issue) issue_one(i + P, fill, q);
-                    }
                     __builtin_amdgcn_sched_barrier(0);
-                }
-                // reads and loads that did not fit between the MFMAs
 #pragma unroll
-                for (int r = (NMF + RGAP - 1) / RGAP; r < NRD; ++r) {
-                    if (!last)
-                        read_one(slot, ks + 1, (ks + 1) & 1, r);
-                    else if (i + 1 < nk)
-                        read_one(next, 0, 0, r);
-                }
-                if (!last) {
+                    for (int m = 0; m < NMF; ++m) {
+                        mfma_one(ks % NB, m);
+                        if (m < NRD) read_one(rslot, tks, tbuf, m);
+                        if (ks < SPREAD && m % LGAP == 0 && m / LGAP < LPK) {
+                            const int q = ks * LPK + m / LGAP;
+                            if (q < LOADS) issue_one(load_chunk, fill, q, valid);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    // reads and loads that did not fit between the MFMAs
 #pragma unroll
-                    for (int u = (NMF + LGAP - 1) / LGAP; u < LPK; ++u) {
-                        const int q = ks * LPK + u;
-                        if (q < LOADS && do_issue) issue_one(i + P, fill, q);
+                    for (int r = NMF; r < NRD; ++r) read_one(rslot, tks, tbuf, r);
+                    if (ks < SPREAD) {
+#pragma unroll
+                        for (int u = (NMF + LGAP - 1) / LGAP; u < LPK; ++u) {
+                            const int q = ks * LPK + u;
+                            if (q < LOADS) issue_one(load_chunk, fill, q, valid);
+                        }
                     }
                 }
+                slot = next;
+                fill = (fill + 1 == SLOTS) ? 0 : fill + 1;
             }
-            slot = next;
-            fill = (fill + 1 == SLOTS) ? 0 : fill + 1;
+            // the zero fills past the last chunk must land before the slots
+            // are reused or the workgroup's LDS is released
+            wait_vmcnt<0>();
         }
     }
 
-    // ---- epilogue.  With the operands swapped, fragment (i, j) holds C^T:
+    // Accumulator registers 4q .. 4q+3 (0 <= q < NREG / 4).
+    __device__ __forceinline__ f32x4v get4(int q) const
+    {
+        constexpr int GR = MM::regs / 4;
+        const int i = q / (FN * GR), j = (q / GR) % FN, g = q % GR;
+        return f32x4v{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+    }
+    __device__ __forceinline__ void set4(int q, f32x4v v)
+    {
+        constexpr int GR = MM::regs / 4;
+        const int i = q / (FN * GR), j = (q / GR) % FN, g = q % GR;
+        acc[i][j][4 * g] = v[0];
+        acc[i][j][4 * g + 1] = v[1];
+        acc[i][j][4 * g + 2] = v[2];
+        acc[i][j][4 * g + 3] = v[3];
+    }
+
+    // Epilogue.  With the operands swapped, fragment (i, j) holds C^T:
     //   MF = 16: value q of lane -> m = lane % 16, n = 4 (lane / 16) + q
     //   MF = 32: value 4 g + q   -> m = lane % 32, n = 8 g + 4 (lane / 32) + q
-    const int64_t M = p.M, N = p.N;
-    const bool vec_ok = (N & 3) == 0;
-    constexpr int GROUPS = MM::regs / 4;
+    // MODE 0..2 store epilogue(acc) rounded to T into C (batch l); MODE_PARTIAL
+    // stores the raw fp32 sums into W ([M][N] for this batch and split).
+    template <int MODE>
+    __device__ __forceinline__ void store(void *out, int64_t M, int64_t N)
+    {
+        const bool vec_ok = (N & 3) == 0;
+        constexpr int GROUPS = MM::regs / 4;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int64_t m = m0 + wm * WTM + i * MF + lrow;
-        if (m >= M) continue;
+        for (int i = 0; i < FM; ++i) {
+            const int64_t m = m0 + wm * WTM + i * MF + lrow;
+            if (m >= M) continue;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
+            for (int j = 0; j < FN; ++j) {
 #pragma unroll
-            for (int g = 0; g < GROUPS; ++g) {
-                const int64_t n = n0 + wn * WTN + j * MF + g * 8 + lcol * 4;
-                const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
-                const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-                if constexpr (MODE == MODE_PARTIAL) {
-                    float *W = reinterpret_cast<float *>(p.C) + ((int64_t)s * p.L + l) * M * N + m * N;
-                    if (vec_ok && n + 3 < N) {
-                        *reinterpret_cast<f32x4v *>(W + n) = f32x4v{v0, v1, v2, v3};
+                for (int g = 0; g < GROUPS; ++g) {
+                    const int64_t n = n0 + wn * WTN + j * MF + g * 8 + lcol * 4;
+                    const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
+                    const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+                    if constexpr (MODE == MODE_PARTIAL) {
+                        float *W = reinterpret_cast<float *>(out) + m * N;
+                        if (vec_ok && n + 3 < N) {
+                            *reinterpret_cast<f32x4v *>(W + n) = f32x4v{v0, v1, v2, v3};
+                        } else {
+                            const float v[4] = {v0, v1, v2, v3};
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                if (n + q < N) W[n + q] = v[q];
+                        }
                     } else {
-                        const float v[4] = {v0, v1, v2, v3};
+                        T *Cr = reinterpret_cast<T *>(out) + m * N;
+                        const float y0 = apply_epilogue<MODE>(v0), y1 = apply_epilogue<MODE>(v1);
+                        const float y2 = apply_epilogue<MODE>(v2), y3 = apply_epilogue<MODE>(v3);
+                        if (vec_ok && n + 3 < N) {
+                            Elem<T>::store4(Cr + n, y0, y1, y2, y3);
+                        } else {
+                            const float y[4] = {y0, y1, y2, y3};
 #pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            if (n + q < N) W[n + q] = v[q];
-                    }
-                } else {
-                    T *Cr = reinterpret_cast<T *>(p.C) + ((int64_t)l * M + m) * N;
-                    const float y0 = apply_epilogue<MODE>(v0), y1 = apply_epilogue<MODE>(v1);
-                    const float y2 = apply_epilogue<MODE>(v2), y3 = apply_epilogue<MODE>(v3);
-                    if (vec_ok && n + 3 < N) {
-                        Elem<T>::store4(Cr + n, y0, y1, y2, y3);
-                    } else {
-                        const float y[4] = {y0, y1, y2, y3};
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            if (n + q < N) Cr[n + q] = Elem<T>::from_f32(y[q]);
+                            for (int q = 0; q < 4; ++q)
+                                if (n + q < N) Cr[n + q] = Elem<T>::from_f32(y[q]);
+                        }
                     }
                 }
             }
         }
+    }
+
+    // A private fp32 copy of the accumulators (a stream-K partial tile), in
+    // register order: group q of 4 floats of thread t at (q * THREADS + t) * 4,
+    // so that every store and load is a coalesced 16-byte access.
+    __device__ __forceinline__ void save_partial(float *W)
+    {
+        const __amdgpu_buffer_rsrc_t r = partial_rsrc(W);
+#pragma unroll
+        for (int q = 0; q < NREG / 4; ++q)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, get4(q)), r,
+                                                   (q * THREADS + (int)threadIdx.x) * 16, 0, kCoherent);
+    }
+
+    // Replace the accumulators by sum_{k < n} piece_k, added in ascending k
+    // from the left; piece `mine` is the accumulators themselves, the others are
+    // saved partials (W_k = ws + slot_k * BM * BN).
+    __device__ __forceinline__ void combine(const float *ws, const int *slots, int n, int mine)
+    {
+#pragma unroll
+        for (int q = 0; q < NREG / 4; ++q) {
+            const f32x4v own = get4(q);
+            f32x4v sum = own;
+            for (int k = 0; k < n; ++k) {
+                f32x4v v = own;
+                if (k != mine)
+                    v = __builtin_bit_cast(
+                        f32x4v, __builtin_amdgcn_raw_buffer_load_b128(
+                                    partial_rsrc(ws + (int64_t)slots[k] * (BM * BN)),
+                                    (q * THREADS + (int)threadIdx.x) * 16, 0, kCoherent));
+                if (k == 0) {
+                    sum = v;
+                } else {
+                    sum[0] += v[0];
+                    sum[1] += v[1];
+                    sum[2] += v[2];
+                    sum[3] += v[3];
+                }
+            }
+            set4(q, sum);
+        }
+    }
+};
+
+// Tile id (within one batch) -> (tm, tn): tiles rastered in groups of group_m
+// tile rows, column-major inside a group.
+__device__ __forceinline__ void raster(int tile, int tiles_m, int tiles_n, int group_m, int &tm, int &tn)
+{
+    const int width = group_m * tiles_n;
+    const int first_m = (tile / width) * group_m;
+    const int gsize = min(tiles_m - first_m, group_m);
+    tm = first_m + (tile % width) % gsize;
+    tn = (tile % width) / gsize;
+}
+
+// Data-parallel / split-K grid: one workgroup per (batch, split, tile).
+template <class T, int BM, int BN, int RB, int WAVES_M, int WAVES_N, int MF, int P, int MODE>
+__global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_tile_kernel(TileParams p)
+{
+    typedef TileCore<T, BM, BN, RB, WAVES_M, WAVES_N, MF, P> Core;
+    __shared__ __attribute__((aligned(1024))) char smem[Core::LDS_BYTES];
+    Core c;
+    c.init(smem);
+
+    // [l][s][tile], after the XCD remap
+    int t = xcd_remap(blockIdx.x, gridDim.x);
+    const int tiles = p.tiles_m * p.tiles_n;
+    const int tile = t % tiles;
+    t /= tiles;
+    const int s = t % p.split;
+    const int l = t / p.split;
+    int tm, tn;
+    raster(tile, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+
+    const int chunk0 = s * p.chunks_per_split;
+    int nk = p.total_chunks - chunk0;
+    if (nk > p.chunks_per_split) nk = p.chunks_per_split;
+    if (nk < 0) nk = 0;
+
+    c.setup(p, l, tm, tn);
+    c.zero();
+    c.run(chunk0, nk);
+    if constexpr (MODE == MODE_PARTIAL)
+        c.template store<MODE>(reinterpret_cast<float *>(p.C) + ((int64_t)s * p.L + l) * p.M * p.N, p.M, p.N);
+    else
+        c.template store<MODE>(reinterpret_cast<T *>(p.C) + (int64_t)l * p.M * p.N, p.M, p.N);
+}
+
+// ------------------------------------------------------------------ stream-K
+
+// The (tile, chunk) units of all tiles, tile-major, are cut into gridDim.x
+// contiguous ranges of equal size (+-1), one per workgroup (the persistent
+// variant of the data-parallel grid).  A tile whose chunks fall into several
+// ranges is summed from the pieces in ascending chunk order by whichever piece
+// finishes last: every other piece leaves its fp32 partial in the workspace
+// and counts itself in the tile's counter.  Pieces, their order and hence the
+// result are fixed by the shape and the grid: bitwise reproducible.
+struct StreamKParams {
+    TileParams t;
+    float *ws;        // 2 * gridDim.x partial tiles of BM * BN floats
+    int *counters;    // one per tile (all batches), zero between calls
+    int64_t units;    // tiles * total_chunks
+};
+
+// First unit of range g, and the range holding unit u.
+__device__ __forceinline__ int64_t range_start(int64_t U, int g, int G) { return U * g / G; }
+__device__ __forceinline__ int range_of(int64_t U, int64_t u, int G) { return (int)(((u + 1) * G - 1) / U); }
+
+template <class T, int BM, int BN, int RB, int WAVES_M, int WAVES_N, int MF, int P, int MODE>
+__global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_streamk_kernel(StreamKParams sp)
+{
+    typedef TileCore<T, BM, BN, RB, WAVES_M, WAVES_N, MF, P> Core;
+    __shared__ __attribute__((aligned(1024))) char smem[Core::LDS_BYTES];
+    __shared__ int s_flag;
+    Core c;
+    c.init(smem);
+    const TileParams &p = sp.t;
+    const int G = gridDim.x;
+    const int g = xcd_remap(blockIdx.x, G);   // neighbouring ranges share an XCD
+    const int64_t U = sp.units;
+    const int C = p.total_chunks;
+    const int tiles = p.tiles_m * p.tiles_n;
+    int64_t u = range_start(U, g, G);
+    const int64_t u_end = range_start(U, g + 1, G);
+    while (u < u_end) {
+        const int64_t tg = u / C;              // global tile index (all batches)
+        const int c0 = (int)(u % C);
+        const int c1 = (int)min((int64_t)C, (int64_t)c0 + (u_end - u));
+        const int l = (int)(tg / tiles);
+        int tm, tn;
+        raster((int)(tg % tiles), p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+        c.setup(p, l, tm, tn);
+        c.zero();
+        c.run(c0, c1 - c0);
+        T *Cl = reinterpret_cast<T *>(p.C) + (int64_t)l * p.M * p.N;
+        if (c0 == 0 && c1 == C) {
+            c.template store<MODE>(Cl, p.M, p.N);
+        } else {
+            // pieces of this tile: ranges g_first .. g_last, in chunk order
+            const int g_first = range_of(U, tg * C, G);
+            const int g_last = range_of(U, tg * C + C - 1, G);
+            const int n = g_last - g_first + 1;
+            const int mine = g - g_first;
+            int slots[8];   // a piece spans at most 8 ranges: ranges hold >= C / 8 units
+            for (int k = 0; k < n && k < 8; ++k) {
+                const int gk = g_first + k;
+                // a range's first piece goes to its slot 0, its last to slot 1
+                slots[k] = 2 * gk + ((range_start(U, gk, G) / C == tg) ? 0 : 1);
+            }
+            int *cnt = sp.counters + tg;
+            // the piece that holds chunk 0 is normally the last to finish: if
+            // every other piece is already in, it need not save its own
+            bool last = false;
+            // Protocol: a piece's partial is written through to memory (system
+            // scope stores), every store has completed (vmcnt 0) before any
+            // thread of the workgroup passes the barrier, and only then is the
+            // tile's device-scope counter incremented; the piece that brings
+            // the count to n - 1 reads the partials back with system-scope
+            // loads, which cannot be served by a stale L2 line.
+            if (c0 == 0) {
+                if (threadIdx.x == 0)
+                    s_flag = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n - 1;
+                __syncthreads();
+                last = s_flag;
+                __syncthreads();
+            }
+            if (!last) {
+                c.save_partial(sp.ws + (int64_t)slots[mine] * (BM * BN));
+                asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+                __syncthreads();
+                if (threadIdx.x == 0)
+                    s_flag = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n - 1;
+                __syncthreads();
+                last = s_flag;
+                __syncthreads();
+            }
+            if (last) {
+                c.combine(sp.ws, slots, n, mine);
+                c.template store<MODE>(Cl, p.M, p.N);
+                if (threadIdx.x == 0)
+                    __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        u += c1 - c0;
     }
 }
 

@@ -9,19 +9,21 @@ void register_f16(std::vector<ConfigEntry> &t, DtypeKernels &k)
     typedef _Float16 T;
     const int d = GEMM_MKL_F16;
     //                  T  BM   BN   RB  waves MF  prefetch depths
-    t.push_back(make_entry<T, 256, 256, 64, 2, 2, 32, 1, 2, 3, 4>(d, 4, "f16 256x256 k32 waves2x2 mfma32"));
-    t.push_back(make_entry<T, 256, 256, 64, 2, 4, 32, 2, 3, 4>(d, 3, "f16 256x256 k32 waves2x4 mfma32"));
-    t.push_back(make_entry<T, 256, 256, 64, 4, 2, 32, 2, 3, 4>(d, 3, "f16 256x256 k32 waves4x2 mfma32"));
-    t.push_back(make_entry<T, 256, 256, 128, 2, 4, 32, 1>(d, 1, "f16 256x256 k64 waves2x4 mfma32"));
-    t.push_back(make_entry<T, 256, 128, 128, 4, 2, 32, 1, 2>(d, 2, "f16 256x128 k64 waves4x2 mfma32"));
-    t.push_back(make_entry<T, 256, 256, 128, 2, 2, 32, 1>(d, 1, "f16 256x256 k64 waves2x2 mfma32"));
-    t.push_back(make_entry<T, 256, 128, 128, 2, 2, 32, 1, 2>(d, 2, "f16 256x128 k64 waves2x2 mfma32"));
-    t.push_back(make_entry<T, 128, 256, 128, 2, 2, 32, 1, 2>(d, 2, "f16 128x256 k64 waves2x2 mfma32"));
-    t.push_back(make_entry<T, 128, 128, 128, 2, 2, 32, 0, 1, 2, 3>(d, 2, "f16 128x128 k64 waves2x2 mfma32"));
-    t.push_back(make_entry<T, 64, 64, 128, 2, 2, 32, 1, 2, 3>(d, 2, "f16 64x64 k64 waves2x2 mfma32"));
-    t.push_back(make_entry<T, 128, 128, 128, 2, 2, 16, 2>(d, 2, "f16 128x128 k64 waves2x2 mfma16"));
-    t.push_back(make_entry<T, 256, 256, 128, 2, 2, 16, 1>(d, 1, "f16 256x256 k64 waves2x2 mfma16"));
-    t.push_back(make_entry<T, 256, 256, 128, 2, 4, 16, 1>(d, 1, "f16 256x256 k64 waves2x4 mfma16"));
+    t.push_back(make_entry<T, 256, 256, 64, 2, 2, 32, 1, 2, 3, 4>(d, 4, 0.47f, "f16 256x256 k32 waves2x2 mfma32"));
+    t.push_back(make_entry<T, 256, 256, 64, 2, 4, 32, 2, 3, 4>(d, 3, 0.46f, "f16 256x256 k32 waves2x4 mfma32"));
+    t.push_back(make_entry<T, 256, 256, 64, 4, 2, 32, 2, 3, 4>(d, 3, 0.46f, "f16 256x256 k32 waves4x2 mfma32"));
+    t.push_back(make_entry<T, 256, 256, 128, 2, 4, 32, 1>(d, 1, 0.45f, "f16 256x256 k64 waves2x4 mfma32"));
+    t.push_back(make_entry<T, 256, 128, 128, 4, 2, 32, 1, 2>(d, 2, 0.42f, "f16 256x128 k64 waves4x2 mfma32"));
+    t.push_back(make_entry<T, 256, 256, 128, 2, 2, 32, 1>(d, 1, 0.4f, "f16 256x256 k64 waves2x2 mfma32"));
+    t.push_back(make_entry<T, 256, 128, 128, 2, 2, 32, 1, 2>(d, 2, 0.4f, "f16 256x128 k64 waves2x2 mfma32"));
+    t.push_back(with_streamk<T, 128, 256, 128, 2, 2, 32, 2>(
+        make_entry<T, 128, 256, 128, 2, 2, 32, 1, 2>(d, 2, 0.4f, "f16 128x256 k64 waves2x2 mfma32")));
+    t.push_back(with_streamk<T, 128, 128, 128, 2, 2, 32, 2, 3>(
+        make_entry<T, 128, 128, 128, 2, 2, 32, 0, 1, 2, 3>(d, 3, 0.4f, "f16 128x128 k64 waves2x2 mfma32")));
+    t.push_back(make_entry<T, 64, 64, 128, 2, 2, 32, 1, 2, 3>(d, 2, 0.22f, "f16 64x64 k64 waves2x2 mfma32"));
+    t.push_back(make_entry<T, 128, 128, 128, 2, 2, 16, 2>(d, 2, 0.3f, "f16 128x128 k64 waves2x2 mfma16"));
+    t.push_back(make_entry<T, 256, 256, 128, 2, 2, 16, 1>(d, 1, 0.4f, "f16 256x256 k64 waves2x2 mfma16"));
+    t.push_back(make_entry<T, 256, 256, 128, 2, 4, 16, 1>(d, 1, 0.40f, "f16 256x256 k64 waves2x4 mfma16"));
     fill_dtype_kernels<T>(k);
 }
 
