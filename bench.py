@@ -27,9 +27,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}   # dense MFMA, 256 CU x 2.4 GHz
 HBM_GBS = 8000.0
+# device code: a change here invalidates the stored counter readings
 KERNEL_SOURCES = ["tiled_dense_gemm_mkl_amd/csrc/gemm_kernels.hpp",
                   "tiled_dense_gemm_mkl_amd/csrc/configs.hpp",
-                  "tiled_dense_gemm_mkl_amd/csrc/gemm_api.hip",
                   "tiled_dense_gemm_mkl_amd/csrc/inst_bf16.hip",
                   "tiled_dense_gemm_mkl_amd/csrc/inst_f16.hip",
                   "tiled_dense_gemm_mkl_amd/csrc/inst_f32.hip"]
@@ -43,46 +43,65 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload_key: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources (else None)."""
+def measured_traffic(workload_key: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter readings
+    (FETCH_SIZE and WRITE_SIZE, scaled by the copy-kernel calibration), if they
+    were taken on the current device code and the same kernel (else None)."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
         return None
     try:
         with open(path) as f:
             d = json.load(f)
-        e = d.get(workload_key)
-        if not e or e.get("source_hash") != source_hash():
+        e = d.get("workloads", {}).get(workload_key)
+        if not e or e.get("source_hash") != source_hash() or e.get("kernel") != kernel:
             return None
         return int(e["bytes_per_launch"])
-    except Exception:
+    except (OSError, ValueError, KeyError, TypeError):
         return None
 
 
-def cpu_baseline(w, A, B):
-    """The oracle as it stands, on this host's cores: full workload, median of 3."""
+def cpu_baseline(w, A, B, budget_s: float = 10.0):
+    """The oracle as it stands, on this host's cores: whole calls on the full
+    workload, repeated until about budget_s seconds of CPU work (at least 3);
+    the median call time gives the rate."""
     import oracle
 
     oracle.load()
     times = []
-    threads = 0
-    for _ in range(3):
+    while len(times) < 3 or (sum(times) < budget_s and len(times) < 200):
         t0 = time.perf_counter()
         y = oracle.gemm64(A, B, w.dtype, w.epilogue)
         times.append(time.perf_counter() - t0)
         del y
     threads = oracle.threads()
-    times.sort()
-    t = times[1]
+    t = sorted(times)[len(times) // 2]
     return {
         "value": round(w.flops / t / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"full workload ({w.M}x{w.N}x{w.K}, L={w.L}), binary64 triple loop, median of 3 runs "
-                  f"({t:.2f} s each)",
+        "sample": f"{len(times)} whole calls on the full workload ({w.M}x{w.N}x{w.K}, L={w.L}), "
+                  f"binary64 dot products, median {t:.3f} s per call",
     }
+
+
+def copy_calibration(mib: int, steps: int) -> int:
+    """A plain device copy of known size (torch.neg, out= a second buffer),
+    launched `steps` times: rocprofv3's FETCH_SIZE / WRITE_SIZE for it give the
+    factor that turns those counters into bytes."""
+    import torch
+
+    dev = torch.device("cuda", 0)
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": True, "bytes_read": n * 4, "bytes_written": n * 4,
+                      "launches": steps}), flush=True)
+    return 0
 
 
 def main() -> int:
@@ -92,14 +111,17 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="run only a device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
               "the GEMM is not sharded across GPUs in this build", file=sys.stderr)
         return 2
+    if args.calibrate_copy:
+        return copy_calibration(args.calibrate_copy, max(1, args.steps))
 
-    import numpy as np
     import torch
 
     import tiled_dense_gemm_mkl_amd as gm
@@ -130,6 +152,11 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
 
+    # HIP events on the stream the kernels run on bracket the K launches: the
+    # launches queue back to back, so their span over K is the average launch
+    # duration the roofline uses (rocprofv3's kernel trace of the same command
+    # shows no idle gap between consecutive launches).  The wall clock over
+    # the same region gives the throughput.
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -140,14 +167,15 @@ def main() -> int:
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ev_ms = start.elapsed_time(end)
     ms_per_step = wall * 1e3 / args.steps
-    ev_ms_per_launch = ev_ms / args.steps
+    ev_ms_per_launch = start.elapsed_time(end) / args.steps
 
     value = w.flops / (ms_per_step * 1e-3) / 1e12
     achieved = w.flops / (ev_ms_per_launch * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = measured_traffic(key)
+    kernel_config = gm.config_names()[plan["config_id"]] if plan["config_id"] >= 0 else "general"
+    kernel = f"{kernel_config} P{plan['prefetch_stages']} S{plan['split_k']}" + (" stream-K" if plan["streamk"] else "")
+    traffic = measured_traffic(key, kernel)
 
     result = {
         "metric": "GEMM TFLOP/s + % of MFMA peak, bf16 M=512 N=5632 K=2048 ReLU, 1 MI355X",
@@ -168,7 +196,7 @@ def main() -> int:
             "epilogue": w.epilogue,
             "plan": {k: plan[k] for k in ("config_id", "prefetch_stages", "split_k", "grid",
                                            "block_m", "block_n", "block_k", "threads")},
-            "kernel_config": gm.config_names()[plan["config_id"]] if plan["config_id"] >= 0 else "general",
+            "kernel": kernel,
         },
         "pct_of_mfma_peak": round(100.0 * value / peak, 2),
         "roofline": {

@@ -123,8 +123,11 @@ int gemm_mkl(const void *A, const void *B, void *C,
  * The environment variables GEMM_MKL_FORCE_CONFIG, GEMM_MKL_STAGES and
  * GEMM_MKL_SPLIT_K supply the same three choices when opts leaves them
  * automatic (for sweeps); GEMM_MKL_STREAMK=0/1/-1 never / always / by model
- * uses stream-K; GEMM_MKL_GROUP_M sets the tile-raster group height; GEMM_MKL_LOG=1 prints each call's plan to stderr;
- * GEMM_MKL_WORKSPACE_LIMIT=<bytes> caps the internal workspace.
+ * uses stream-K; GEMM_MKL_GROUP_M sets the tile-raster group height;
+ * GEMM_MKL_LOG=1 prints each call's plan to stderr;
+ * GEMM_MKL_WORKSPACE_LIMIT=<bytes> caps the internal workspace.  They are
+ * read once, at the first call.  Plans are cached per (sizes, dtype, pointer
+ * alignment, options), so a repeated call does no planning work.
  */
 typedef struct gemm_mkl_opts {
     int32_t prefetch_stages; /* -1 = auto */

@@ -58,6 +58,30 @@ int env_int(const char *name, int dflt)
     return std::atoi(v);
 }
 
+// The environment overrides, read once, at the first call that needs them.
+struct EnvSettings {
+    int force_config, stages, split_k, streamk, group_m, log;
+    bool has_ws_limit;
+    size_t ws_limit;
+    EnvSettings()
+        : force_config(env_int("GEMM_MKL_FORCE_CONFIG", -1)), stages(env_int("GEMM_MKL_STAGES", -1)),
+          split_k(env_int("GEMM_MKL_SPLIT_K", 0)), streamk(env_int("GEMM_MKL_STREAMK", 0)),
+          group_m(env_int("GEMM_MKL_GROUP_M", 4)), log(env_int("GEMM_MKL_LOG", 0)), has_ws_limit(false), ws_limit(0)
+    {
+        const char *lim = std::getenv("GEMM_MKL_WORKSPACE_LIMIT");
+        if (lim && *lim) {
+            has_ws_limit = true;
+            ws_limit = (size_t)std::strtoull(lim, nullptr, 10);
+        }
+    }
+};
+
+const EnvSettings &env()
+{
+    static const EnvSettings e;
+    return e;
+}
+
 bool mul_ok(int64_t a, int64_t b, int64_t *out)
 {
     if (a < 0 || b < 0) return false;
@@ -183,15 +207,15 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
     Registry &R = registry();
     const int64_t es = elem_bytes(dtype);
     int forced_cfg = o ? o->config_id : -1;
-    if (forced_cfg < 0) forced_cfg = env_int("GEMM_MKL_FORCE_CONFIG", -1);
+    if (forced_cfg < 0) forced_cfg = env().force_config;
     int forced_p = o ? o->prefetch_stages : -1;
-    if (forced_p < 0) forced_p = env_int("GEMM_MKL_STAGES", -1);
+    if (forced_p < 0) forced_p = env().stages;
     int forced_s = o ? o->split_k : 0;
-    if (forced_s <= 0) forced_s = env_int("GEMM_MKL_SPLIT_K", 0);
+    if (forced_s <= 0) forced_s = env().split_k;
     const bool force_general = o && (o->flags & GEMM_MKL_OPT_FORCE_GENERAL);
     // stream-K: -1 automatic, 0 never, 1 always (where a configuration has it)
     // (automatic choice is off until the stream-K fix-up beats the data-parallel grid)
-    int sk_mode = env_int("GEMM_MKL_STREAMK", 0);
+    int sk_mode = env().streamk;
     if (o && (o->flags & GEMM_MKL_OPT_STREAMK)) sk_mode = 1;
     if (o && (o->flags & GEMM_MKL_OPT_NO_STREAMK)) sk_mode = 0;
     // an explicit split_k selects the split-K grid (1: no split of K at all);
@@ -292,7 +316,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
     }
     // raster groups of up to 4 tile rows: the 32 workgroups an XCD runs at
     // once then share few A row-blocks and B column-blocks in its L2
-    plan->group_m = std::min<int32_t>(plan->tiles_m, (int32_t)env_int("GEMM_MKL_GROUP_M", 4));
+    plan->group_m = std::min<int32_t>(plan->tiles_m, (int32_t)env().group_m);
     if (plan->group_m < 1) plan->group_m = 1;
     plan->grid = (int64_t)plan->tiles_m * plan->tiles_n * plan->S * L;
     if (plan->grid > INT32_MAX) return GEMM_MKL_STATUS_NOT_AVAILABLE;
@@ -307,6 +331,54 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
         plan->ws_bytes = plan->sk_counter_bytes + (size_t)2 * plan->grid * c.bm * c.bn * 4;
     }
     return GEMM_MKL_STATUS_OK;
+}
+
+// Plans depend only on the sizes, the dtype, pointer alignment and the
+// options, so each distinct request is planned once and then looked up.
+struct PlanKey {
+    int64_t M, N, K, L;
+    int32_t dtype, aligned, config_id, prefetch, split, flags;
+    bool operator<(const PlanKey &o) const
+    {
+        return std::memcmp(this, &o, sizeof(PlanKey)) < 0;
+    }
+};
+static_assert(sizeof(PlanKey) == 56, "PlanKey must have no padding (compared bytewise)");
+
+std::mutex g_plan_mutex;
+std::map<PlanKey, std::pair<int, Plan>> g_plans;
+constexpr size_t kMaxCachedPlans = 4096;
+
+int cached_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_mkl_opts *o, bool aligned,
+                Plan *plan)
+{
+    PlanKey key;
+    std::memset(&key, 0, sizeof key);
+    key.M = M;
+    key.N = N;
+    key.K = K;
+    key.L = L;
+    key.dtype = dtype;
+    key.aligned = aligned ? 1 : 0;
+    key.config_id = o ? o->config_id : -1;
+    key.prefetch = o ? o->prefetch_stages : -1;
+    key.split = o ? o->split_k : 0;
+    key.flags = o ? o->flags : 0;
+    {
+        std::lock_guard<std::mutex> g(g_plan_mutex);
+        auto it = g_plans.find(key);
+        if (it != g_plans.end()) {
+            *plan = it->second.second;
+            return it->second.first;
+        }
+    }
+    Plan fresh;
+    const int st = make_plan(M, N, K, L, dtype, o, aligned, &fresh);
+    std::lock_guard<std::mutex> g(g_plan_mutex);
+    if (g_plans.size() >= kMaxCachedPlans) g_plans.clear();
+    g_plans.emplace(key, std::make_pair(st, fresh));
+    *plan = fresh;
+    return st;
 }
 
 // ---------------------------------------------------------------- internal workspace
@@ -370,8 +442,7 @@ int get_workspace(hipStream_t stream, size_t need, void **out)
         t_last_hip = e;
         return GEMM_MKL_STATUS_HIP_ERROR;
     }
-    const char *lim = std::getenv("GEMM_MKL_WORKSPACE_LIMIT");
-    if (lim && *lim && need > (size_t)std::strtoull(lim, nullptr, 10)) return GEMM_MKL_STATUS_WORKSPACE;
+    if (env().has_ws_limit && need > env().ws_limit) return GEMM_MKL_STATUS_WORKSPACE;
     std::lock_guard<std::mutex> g(g_ws_mutex);
     Workspace &w = g_ws[std::make_pair(dev, stream)];
     if (w.bytes < need) {
@@ -413,12 +484,12 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
     const bool aligned = al(A, 16) && al(B, 16) && al(C, 4 * es);
 
     Plan plan;
-    st = make_plan(M, N, K, L, dtype, o, aligned, &plan);
+    st = cached_plan(M, N, K, L, dtype, o, aligned, &plan);
     if (st != GEMM_MKL_STATUS_OK) return st;
 
     Registry &R = registry();
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
-    if (env_int("GEMM_MKL_LOG", 0))
+    if (env().log)
         std::fprintf(stderr, "gemm_mkl: M=%lld N=%lld K=%lld L=%lld dtype=%d epi=%d -> %s P=%d S=%d%s grid=%lld\n",
                      (long long)M, (long long)N, (long long)K, (long long)L, dtype, epilogue,
                      plan.general ? "general" : R.table[plan.config_id].name, plan.P, plan.S,
@@ -524,7 +595,7 @@ int gemm_mkl_get_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, int
         return GEMM_MKL_STATUS_OK;
     }
     Plan plan;
-    st = make_plan(M, N, K, L, dtype, opts, true, &plan);
+    st = cached_plan(M, N, K, L, dtype, opts, true, &plan);
     if (st != GEMM_MKL_STATUS_OK) return st;
     out->config_id = plan.config_id;
     out->prefetch_stages = plan.P;
