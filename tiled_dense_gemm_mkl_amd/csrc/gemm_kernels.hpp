@@ -38,6 +38,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace gmk {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -209,6 +211,12 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 }
 
+// Plain workgroup barrier (the waves' own waits precede it).
+__device__ __forceinline__ void block_barrier()
+{
+    asm volatile("s_barrier" : : : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p)
 {
     return (uint32_t)reinterpret_cast<uintptr_t>(p);
@@ -332,16 +340,21 @@ struct TileCore {
     static constexpr int RA = (NMF >= 8 || KSTEPS < 4) ? 1 : KSTEPS - 1;
     static constexpr int NB = RA + 1;
     static_assert(KSTEPS % NB == 0, "fragment ring must divide the k-steps of a chunk");
-    // Chunk i + 1 is waited for at k-step WIN of chunk i.  The loads of chunk
-    // i + P are spread over the first SPREAD k-steps of chunk i: all of them
-    // (P >= 2, the wait then allows for the QW of them issued before k-step WIN)
-    // or, with P = 1 where chunk i + P is the one waited for, only those before
-    // the wait.
+    // P >= 2: one wait and one barrier per chunk, at the chunk boundary.  At
+    // the end of chunk i every wave has issued all MFMAs of chunk i (so its
+    // reads of slot i are complete) and chunk i + 2 must be visible (its first
+    // RA k-steps are read during chunk i + 1); the loads of chunk i + 1 + P,
+    // spread over all k-steps of chunk i + 1, then refill slot i.  In flight
+    // at the wait: the loads of chunks i + 3 .. i + P.
+    // P == 1: chunk i + 1 is loaded during chunk i itself, so it is waited for
+    // at k-step WIN = KSTEPS - RA of chunk i, just before its first reads; the
+    // loads are spread over the k-steps before the wait, and the barrier there
+    // also drains this wave's reads of chunk i (slot i - 1 ... is refilled from
+    // the next chunk on).
     static constexpr int WIN = KSTEPS - RA;
     static constexpr int SPREAD = P >= 2 ? KSTEPS : WIN;
     static constexpr int LPK = (LOADS + SPREAD - 1) / SPREAD;      // loads per k-step
-    static constexpr int QW = (WIN * LPK < LOADS) ? WIN * LPK : LOADS;
-    static constexpr int WAIT_CNT = P >= 2 ? LOADS * (P - 2) + QW : 0;
+    static constexpr int WAIT_CNT = P >= 2 ? LOADS * (P - 2) : 0;
     static_assert(RB == 64 || RB == 128, "row bytes");
     static_assert(MF == 16 || MF == 32, "MFMA shape");
     static_assert(BM % (MF * WAVES_M) == 0 && BN % (MF * WAVES_N) == 0, "wave tile");
@@ -349,7 +362,6 @@ struct TileCore {
     static_assert(KSTEPS >= 2 && KSTEPS % 2 == 0, "k-steps per chunk: even, for the register double buffer");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 workgroup");
     static_assert(LOADS * (P > 0 ? P : 1) < 64, "vmcnt range");
-    static_assert(P < 2 || WAIT_CNT < LOADS * (P - 1) + 1, "wait count");
 
     char *smem;
     uint32_t smem_base;
@@ -484,6 +496,41 @@ struct TileCore {
         acc[i][j] = MM::step(fb[buf][j], fa[buf][i], acc[i][j]);
     }
 
+    // One k-step of chunk i (in `slot`): its MFMAs, interleaved with the
+    // fragment reads of the k-step RA ahead (in `next` past the chunk's end)
+    // and, in the first SPREAD k-steps, the loads of chunk `load_chunk` into
+    // slot `fill`.
+    __device__ __forceinline__ void step(int ks, int slot, int next, int fill, int load_chunk, bool valid)
+    {
+        constexpr int LGAP = (NMF / LPK) > 0 ? (NMF / LPK) : 1;    // MFMAs between loads
+        const int t = ks + RA;                 // k-step whose fragments are read now
+        const bool in_next = t >= KSTEPS;      // ... of the next chunk
+        const int tks = in_next ? t - KSTEPS : t;
+        const int tbuf = t % NB;
+        const int rslot = in_next ? next : slot;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < NMF; ++m) {
+            mfma_one(ks % NB, m);
+            if (m < NRD) read_one(rslot, tks, tbuf, m);
+            if (ks < SPREAD && m % LGAP == 0 && m / LGAP < LPK) {
+                const int q = ks * LPK + m / LGAP;
+                if (q < LOADS) issue_one(load_chunk, fill, q, valid);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // reads and loads that did not fit between the MFMAs
+#pragma unroll
+        for (int r = NMF; r < NRD; ++r) read_one(rslot, tks, tbuf, r);
+        if (ks < SPREAD) {
+#pragma unroll
+            for (int u = (NMF + LGAP - 1) / LGAP; u < LPK; ++u) {
+                const int q = ks * LPK + u;
+                if (q < LOADS) issue_one(load_chunk, fill, q, valid);
+            }
+        }
+    }
+
     // acc += sum over chunks [c_begin, c_begin + nk) of the tile.  On entry no
     // load of this workgroup is in flight; on exit none is, and every wave is
     // past its last LDS read of the range.
@@ -504,26 +551,23 @@ struct TileCore {
                     for (int t = 0; t < NMF; ++t) mfma_one(ks & 1, t);
                 }
             }
-        } else if (nk > 0) {
+        } else {
+            if (nk <= 0) return;
             // The ring.  During iteration i (consuming chunk i from slot i mod
             // SLOTS) the loads of chunk i + P go to slot (i + P) mod SLOTS, the
-            // slot chunk i - 1 used, spread between the MFMAs of the first WIN
-            // k-steps.  At k-step WIN of chunk i, chunk i + 1 is waited for and
-            // a barrier makes every wave's part of it visible and retires every
-            // wave's reads of chunk i (all issued by then: reads run RA steps
-            // ahead); the fragments of chunk i + 1's first RA k-steps are then
-            // read under the last MFMAs of chunk i.
+            // slot chunk i - 1 used; fragment reads run RA k-steps ahead of
+            // their MFMAs, into chunk i + 1 during the last RA k-steps.
             //
             // The loop body has no branches, so that the compiler can count
             // the LDS reads in flight exactly: past the last chunk the loads
             // become zero fills of the free slot (valid == false) and the reads
             // of the chunk after the last one land in registers that are never
-            // used.  Exactly P chunks of loads are always in flight after a
-            // chunk's wait, hence one vmcnt value for every wait.
-            constexpr int LGAP = (NMF / LPK) > 0 ? (NMF / LPK) : 1;    // MFMAs between loads
+            // used.  Every wait sees the same number of loads issued after the
+            // chunk it waits for, hence one vmcnt value for every wait.
 #pragma unroll
             for (int c = 0; c < P; ++c) issue(c_begin + min(c, nk - 1), c, c < nk);
-            wait_vmcnt<LOADS * (P - 1)>();
+            // chunks 0 and 1 (P >= 2), or chunk 0 (P == 1), have landed
+            wait_vmcnt<LOADS * (P - 1) - (P >= 2 ? LOADS : 0)>();
             lds_barrier();
 #pragma unroll
             for (int ks = 0; ks < RA; ++ks)
@@ -537,39 +581,19 @@ struct TileCore {
                 const int load_chunk = c_begin + min(i + P, nk - 1);
 #pragma unroll
                 for (int ks = 0; ks < KSTEPS; ++ks) {
-                    const int t = ks + RA;                 // k-step whose fragments are read now
-                    const bool in_next = t >= KSTEPS;      // ... of chunk i + 1
-                    const int tks = in_next ? t - KSTEPS : t;
-                    const int tbuf = t % NB;
-                    const int rslot = in_next ? next : slot;
-                    if (ks == WIN) {
-                        // chunk i + 1 has landed once at most the loads issued
-                        // after it are in flight: chunks i + 2 .. i + P - 1 and
-                        // the first QW loads of chunk i + P
-                        wait_vmcnt<WAIT_CNT>();
-                        lds_barrier();
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int m = 0; m < NMF; ++m) {
-                        mfma_one(ks % NB, m);
-                        if (m < NRD) read_one(rslot, tks, tbuf, m);
-                        if (ks < SPREAD && m % LGAP == 0 && m / LGAP < LPK) {
-                            const int q = ks * LPK + m / LGAP;
-                            if (q < LOADS) issue_one(load_chunk, fill, q, valid);
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                    // reads and loads that did not fit between the MFMAs
-#pragma unroll
-                    for (int r = NMF; r < NRD; ++r) read_one(rslot, tks, tbuf, r);
-                    if (ks < SPREAD) {
-#pragma unroll
-                        for (int u = (NMF + LGAP - 1) / LGAP; u < LPK; ++u) {
-                            const int q = ks * LPK + u;
-                            if (q < LOADS) issue_one(load_chunk, fill, q, valid);
+                    if constexpr (P == 1) {
+                        if (ks == WIN) {
+                            // chunk i + 1 (all its loads were issued before
+                            // k-step WIN) has landed
+                            wait_vmcnt<0>();
+                            lds_barrier();
                         }
                     }
+                    step(ks, slot, next, fill, load_chunk, valid);
+                }
+                if constexpr (P >= 2) {
+                    wait_vmcnt<WAIT_CNT>();
+                    block_barrier();
                 }
                 slot = next;
                 fill = (fill + 1 == SLOTS) ? 0 : fill + 1;
@@ -604,6 +628,78 @@ struct TileCore {
     // stores the raw fp32 sums into W ([M][N] for this batch and split).
     template <int MODE>
     __device__ __forceinline__ void store(void *out, int64_t M, int64_t N)
+    {
+        typedef typename std::conditional<MODE == MODE_PARTIAL, float, T>::type OT;
+        if constexpr (BM * BN * (int)sizeof(OT) <= LDS_BYTES)
+            store_staged<MODE, OT>(reinterpret_cast<OT *>(out), M, N);
+        else
+            store_direct<MODE>(out, M, N);
+    }
+
+    // The finished tile (epilogue applied, converted to the output type OT)
+    // goes to LDS row-major, each row's 16-byte columns XOR-swizzled by the
+    // row index; it is then stored with one 16-byte access per lane, lanes
+    // running along rows, so that every store instruction writes whole cache
+    // lines instead of 8 bytes in each of 32 rows.
+    template <int MODE, class OT>
+    __device__ __forceinline__ void store_staged(OT *out, int64_t M, int64_t N)
+    {
+        constexpr int OES = (int)sizeof(OT);
+        constexpr int ROWB = BN * OES;          // bytes per tile row
+        constexpr int NC = ROWB / 16;           // 16-byte columns per row
+        constexpr int EPC = 16 / OES;           // elements per 16-byte column
+        constexpr int RPP = THREADS / NC;       // rows per pass of the workgroup
+        constexpr int GROUPS = MM::regs / 4;
+        static_assert(ROWB % 16 == 0 && THREADS % NC == 0 && BM % RPP == 0, "staged store layout");
+        lds_barrier();   // every wave's ring reads and loads are done
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int r = wm * WTM + i * MF + lrow;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                for (int g = 0; g < GROUPS; ++g) {
+                    const int cn = wn * WTN + j * MF + g * 8 + lcol * 4;   // first of 4 columns
+                    float y[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float v = acc[i][j][4 * g + q];
+                        y[q] = (MODE == MODE_PARTIAL) ? v : apply_epilogue<MODE>(v);
+                    }
+                    const int byte = cn * OES;
+                    char *dst = smem + r * ROWB + ((((byte >> 4) ^ (r % NC)) << 4) | (byte & 15));
+                    if constexpr (OES == 4)
+                        *reinterpret_cast<f32x4v *>(dst) = f32x4v{y[0], y[1], y[2], y[3]};
+                    else
+                        Elem<T>::store4(reinterpret_cast<T *>(dst), y[0], y[1], y[2], y[3]);
+                }
+            }
+        }
+        lds_barrier();   // the whole tile is in LDS
+        const int t = threadIdx.x;
+        const int c = t % NC;
+        const bool vec16 = ((N * OES) & 15) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+#pragma unroll
+        for (int rr = t / NC; rr < BM; rr += RPP) {
+            const i32x4 v = *reinterpret_cast<const i32x4 *>(smem + rr * ROWB + ((c ^ (rr % NC)) << 4));
+            const int64_t gm = m0 + rr;
+            const int64_t gn = n0 + c * EPC;
+            if (gm >= M) continue;
+            OT *dst = out + gm * N + gn;
+            if (vec16 && gn + EPC <= N) {
+                *reinterpret_cast<i32x4 *>(dst) = v;
+            } else {
+                OT e[EPC];
+                __builtin_memcpy(e, &v, 16);
+#pragma unroll
+                for (int q = 0; q < EPC; ++q)
+                    if (gn + q < N) dst[q] = e[q];
+            }
+        }
+    }
+
+    template <int MODE>
+    __device__ __forceinline__ void store_direct(void *out, int64_t M, int64_t N)
     {
         const bool vec_ok = (N & 3) == 0;
         constexpr int GROUPS = MM::regs / 4;
@@ -663,27 +759,43 @@ struct TileCore {
     // saved partials (W_k = ws + slot_k * BM * BN).
     __device__ __forceinline__ void combine(const float *ws, const int *slots, int n, int mine)
     {
+        // Blocks of QB register groups: all loads of one piece's block are
+        // issued before any of them is used, so a piece costs one memory
+        // round trip per block, not one per register group.
+        constexpr int NQ = NREG / 4;
+        constexpr int QB = NQ < 16 ? NQ : 16;
+        static_assert(NQ % QB == 0, "register blocks");
 #pragma unroll
-        for (int q = 0; q < NREG / 4; ++q) {
-            const f32x4v own = get4(q);
-            f32x4v sum = own;
+        for (int q0 = 0; q0 < NQ; q0 += QB) {
+            f32x4v sum[QB];
             for (int k = 0; k < n; ++k) {
-                f32x4v v = own;
-                if (k != mine)
-                    v = __builtin_bit_cast(
-                        f32x4v, __builtin_amdgcn_raw_buffer_load_b128(
-                                    partial_rsrc(ws + (int64_t)slots[k] * (BM * BN)),
-                                    (q * THREADS + (int)threadIdx.x) * 16, 0, kCoherent));
-                if (k == 0) {
-                    sum = v;
+                f32x4v v[QB];
+                if (k == mine) {
+#pragma unroll
+                    for (int b = 0; b < QB; ++b) v[b] = get4(q0 + b);
                 } else {
-                    sum[0] += v[0];
-                    sum[1] += v[1];
-                    sum[2] += v[2];
-                    sum[3] += v[3];
+                    const __amdgpu_buffer_rsrc_t r = partial_rsrc(ws + (int64_t)slots[k] * (BM * BN));
+#pragma unroll
+                    for (int b = 0; b < QB; ++b)
+                        v[b] = __builtin_bit_cast(
+                            f32x4v, __builtin_amdgcn_raw_buffer_load_b128(
+                                        r, ((q0 + b) * THREADS + (int)threadIdx.x) * 16, 0, kCoherent));
+                }
+                if (k == 0) {
+#pragma unroll
+                    for (int b = 0; b < QB; ++b) sum[b] = v[b];
+                } else {
+#pragma unroll
+                    for (int b = 0; b < QB; ++b) {
+                        sum[b][0] += v[b][0];
+                        sum[b][1] += v[b][1];
+                        sum[b][2] += v[b][2];
+                        sum[b][3] += v[b][3];
+                    }
                 }
             }
-            set4(q, sum);
+#pragma unroll
+            for (int b = 0; b < QB; ++b) set4(q0 + b, sum[b]);
         }
     }
 };
