@@ -308,11 +308,17 @@ template <class T> struct Mfma<T, 32> {
 //   RB      bytes of K per row in one chunk (the K-outer step)
 //   MF      MFMA block edge: 32 (v_mfma_f32_32x32x16 / 32x32x2f32) or 16
 //   P       prefetch_stages: chunks in flight ahead of the one consumed
-template <class T, int BM, int BN, int RB, int WAVES_M, int WAVES_N, int MF, int P>
+//   WK      wave groups along K: group kg computes the whole wave tile over
+//           its share of every chunk's k-steps (k-steps kg * KSW .. + KSW - 1),
+//           so each group reads each operand fragment once; the groups' sums
+//           are added in ascending kg before the epilogue.  A chunk's LDS
+//           reads per MFMA fall by WK at the cost of one cross-wave reduction.
+template <class T, int BM, int BN, int RB, int WAVES_M, int WAVES_N, int MF, int P, int WK = 1>
 struct TileCore {
     typedef Mfma<T, MF> MM;
     typedef typename MM::acc_t acc_t;
-    static constexpr int NW = WAVES_M * WAVES_N;
+    static constexpr int NWT = WAVES_M * WAVES_N;        // waves of one k-group
+    static constexpr int NW = NWT * WK;
     static constexpr int THREADS = NW * 64;
     static constexpr int ES = Elem<T>::bytes;
     static constexpr int NCH = RB / 16;                  // 16-byte columns per row
@@ -322,7 +328,8 @@ struct TileCore {
     static constexpr int FM = WTM / MF;
     static constexpr int FN = WTN / MF;
     static constexpr int STEP_COLS = 64 / MF;            // 16-byte columns one MFMA k-step reads per row
-    static constexpr int KSTEPS = NCH / STEP_COLS;
+    static constexpr int KSTEPS = NCH / STEP_COLS;       // MFMA k-steps of a chunk
+    static constexpr int KSW = KSTEPS / WK;              // ... per wave
     static constexpr int SLOTS = P + 1;
     static constexpr int SLOT_BYTES = (BM + BN) * RB;
     static constexpr int LDS_BYTES = SLOTS * SLOT_BYTES;
@@ -336,10 +343,10 @@ struct TileCore {
     static constexpr int NREG = FM * FN * MM::regs;      // accumulator floats per lane
     // Fragment reads run RA k-steps ahead of their MFMAs, in a ring of NB = RA + 1
     // register buffers: one k-step of MFMAs covers the LDS latency when it holds
-    // at least 8 MFMAs; smaller wave tiles read KSTEPS - 1 steps ahead.
-    static constexpr int RA = (NMF >= 8 || KSTEPS < 4) ? 1 : KSTEPS - 1;
+    // at least 8 MFMAs; smaller wave tiles read KSW - 1 steps ahead.
+    static constexpr int RA = (NMF >= 8 || KSW < 4) ? 1 : KSW - 1;
     static constexpr int NB = RA + 1;
-    static_assert(KSTEPS % NB == 0, "fragment ring must divide the k-steps of a chunk");
+    static_assert(KSW % NB == 0, "fragment ring must divide a wave's k-steps of a chunk");
     // P >= 2: one wait and one barrier per chunk, at the chunk boundary.  At
     // the end of chunk i every wave has issued all MFMAs of chunk i (so its
     // reads of slot i are complete) and chunk i + 2 must be visible (its first
@@ -347,25 +354,27 @@ struct TileCore {
     // spread over all k-steps of chunk i + 1, then refill slot i.  In flight
     // at the wait: the loads of chunks i + 3 .. i + P.
     // P == 1: chunk i + 1 is loaded during chunk i itself, so it is waited for
-    // at k-step WIN = KSTEPS - RA of chunk i, just before its first reads; the
+    // at k-step WIN = KSW - RA of chunk i, just before its first reads; the
     // loads are spread over the k-steps before the wait, and the barrier there
     // also drains this wave's reads of chunk i (slot i - 1 ... is refilled from
     // the next chunk on).
-    static constexpr int WIN = KSTEPS - RA;
-    static constexpr int SPREAD = P >= 2 ? KSTEPS : WIN;
+    static constexpr int WIN = KSW - RA;
+    static constexpr int SPREAD = P >= 2 ? KSW : WIN;
     static constexpr int LPK = (LOADS + SPREAD - 1) / SPREAD;      // loads per k-step
     static constexpr int WAIT_CNT = P >= 2 ? LOADS * (P - 2) : 0;
     static_assert(RB == 64 || RB == 128, "row bytes");
     static_assert(MF == 16 || MF == 32, "MFMA shape");
     static_assert(BM % (MF * WAVES_M) == 0 && BN % (MF * WAVES_N) == 0, "wave tile");
     static_assert(A_GROUPS % NW == 0 && B_GROUPS % NW == 0, "load split");
-    static_assert(KSTEPS >= 2 && KSTEPS % 2 == 0, "k-steps per chunk: even, for the register double buffer");
+    static_assert(KSTEPS % WK == 0 && KSW >= 2 && KSW % 2 == 0,
+                  "k-steps per wave and chunk: even, for the register double buffer");
+    static_assert(WK == 1 || NWT * NREG * 256 <= LDS_BYTES, "LDS for the cross-group reduction");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 workgroup");
     static_assert(LOADS * (P > 0 ? P : 1) < 64, "vmcnt range");
 
     char *smem;
     uint32_t smem_base;
-    int lane, wave, wm, wn, lrow, lcol, sw;
+    int lane, wave, wm, wn, kg, lrow, lcol, sw;
     uint32_t rd_a, rd_b;
     int64_t m0, n0, k_bytes;
     int l;
@@ -381,8 +390,9 @@ struct TileCore {
         smem_base = lds_addr(lds);
         lane = threadIdx.x & 63;
         wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        wm = wave % WAVES_M;
-        wn = wave / WAVES_M;
+        kg = wave / NWT;
+        wm = (wave % NWT) % WAVES_M;
+        wn = (wave % NWT) / WAVES_M;
         // operand reads: lane reads row (lane % MF) of each fragment at logical
         // column ks * STEP_COLS + lane / MF
         lrow = lane % MF;
@@ -483,7 +493,7 @@ struct TileCore {
     __device__ __forceinline__ void read_one(int slot, int ks, int buf, int r)
     {
         const char *base = smem + slot * SLOT_BYTES;
-        const int col = ((ks * STEP_COLS + lcol) ^ sw) * 16;
+        const int col = (((kg * KSW + ks) * STEP_COLS + lcol) ^ sw) * 16;
         if (r < FM)
             fa[buf][r] = *reinterpret_cast<const i32x4 *>(base + rd_a + r * MF * RB + col);
         else
@@ -504,8 +514,8 @@ struct TileCore {
     {
         constexpr int LGAP = (NMF / LPK) > 0 ? (NMF / LPK) : 1;    // MFMAs between loads
         const int t = ks + RA;                 // k-step whose fragments are read now
-        const bool in_next = t >= KSTEPS;      // ... of the next chunk
-        const int tks = in_next ? t - KSTEPS : t;
+        const bool in_next = t >= KSW;         // ... of the next chunk
+        const int tks = in_next ? t - KSW : t;
         const int tbuf = t % NB;
         const int rslot = in_next ? next : slot;
         __builtin_amdgcn_sched_barrier(0);
@@ -544,7 +554,7 @@ struct TileCore {
                 wait_vmcnt<0>();
                 lds_barrier();              // every wave's part of chunk i has landed
 #pragma unroll
-                for (int ks = 0; ks < KSTEPS; ++ks) {
+                for (int ks = 0; ks < KSW; ++ks) {
 #pragma unroll
                     for (int r = 0; r < NRD; ++r) read_one(0, ks, ks & 1, r);
 #pragma unroll
@@ -580,7 +590,7 @@ struct TileCore {
                 const bool valid = i + P < nk;
                 const int load_chunk = c_begin + min(i + P, nk - 1);
 #pragma unroll
-                for (int ks = 0; ks < KSTEPS; ++ks) {
+                for (int ks = 0; ks < KSW; ++ks) {
                     if constexpr (P == 1) {
                         if (ks == WIN) {
                             // chunk i + 1 (all its loads were issued before
@@ -626,9 +636,42 @@ struct TileCore {
     //   MF = 32: value 4 g + q   -> m = lane % 32, n = 8 g + 4 (lane / 32) + q
     // MODE 0..2 store epilogue(acc) rounded to T into C (batch l); MODE_PARTIAL
     // stores the raw fp32 sums into W ([M][N] for this batch and split).
+    // WK > 1: the accumulators of k-group 0 become the sum over the groups,
+    // added in ascending kg through LDS (groups 1 .. WK - 1 one at a time).
+    __device__ __forceinline__ void reduce_k()
+    {
+        if constexpr (WK > 1) {
+            constexpr int NQ = NREG / 4;
+            const int wl = wave % NWT;
+#pragma unroll 1
+            for (int k = 1; k < WK; ++k) {
+                lds_barrier();   // the ring (or the previous round) is no longer read
+                if (kg == k) {
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q)
+                        *reinterpret_cast<f32x4v *>(smem + ((wl * NQ + q) * 64 + lane) * 16) = get4(q);
+                }
+                lds_barrier();
+                if (kg == 0) {
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q) {
+                        const f32x4v o = *reinterpret_cast<const f32x4v *>(smem + ((wl * NQ + q) * 64 + lane) * 16);
+                        f32x4v v = get4(q);
+                        v[0] += o[0];
+                        v[1] += o[1];
+                        v[2] += o[2];
+                        v[3] += o[3];
+                        set4(q, v);
+                    }
+                }
+            }
+        }
+    }
+
     template <int MODE>
     __device__ __forceinline__ void store(void *out, int64_t M, int64_t N)
     {
+        reduce_k();
         typedef typename std::conditional<MODE == MODE_PARTIAL, float, T>::type OT;
         if constexpr (BM * BN * (int)sizeof(OT) <= LDS_BYTES)
             store_staged<MODE, OT>(reinterpret_cast<OT *>(out), M, N);
@@ -654,6 +697,7 @@ struct TileCore {
         lds_barrier();   // every wave's ring reads and loads are done
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
+            if (kg != 0) break;   // (k-group 0 holds the sums)
             const int r = wm * WTM + i * MF + lrow;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
@@ -701,6 +745,7 @@ struct TileCore {
     template <int MODE>
     __device__ __forceinline__ void store_direct(void *out, int64_t M, int64_t N)
     {
+        if (kg != 0) return;   // (k-group 0 holds the sums)
         const bool vec_ok = (N & 3) == 0;
         constexpr int GROUPS = MM::regs / 4;
 #pragma unroll
@@ -747,6 +792,7 @@ struct TileCore {
     // so that every store and load is a coalesced 16-byte access.
     __device__ __forceinline__ void save_partial(float *W)
     {
+        static_assert(WK == 1, "stream-K pieces keep one k-group");
         const __amdgpu_buffer_rsrc_t r = partial_rsrc(W);
 #pragma unroll
         for (int q = 0; q < NREG / 4; ++q)
@@ -812,10 +858,10 @@ __device__ __forceinline__ void raster(int tile, int tiles_m, int tiles_n, int g
 }
 
 // Data-parallel / split-K grid: one workgroup per (batch, split, tile).
-template <class T, int BM, int BN, int RB, int WAVES_M, int WAVES_N, int MF, int P, int MODE>
-__global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_tile_kernel(TileParams p)
+template <class T, int BM, int BN, int RB, int WAVES_M, int WAVES_N, int MF, int P, int MODE, int WK = 1>
+__global__ __launch_bounds__(WAVES_M *WAVES_N *WK * 64) void gemm_tile_kernel(TileParams p)
 {
-    typedef TileCore<T, BM, BN, RB, WAVES_M, WAVES_N, MF, P> Core;
+    typedef TileCore<T, BM, BN, RB, WAVES_M, WAVES_N, MF, P, WK> Core;
     __shared__ __attribute__((aligned(1024))) char smem[Core::LDS_BYTES];
     Core c;
     c.init(smem);

@@ -20,6 +20,11 @@ void register_bf16(std::vector<ConfigEntry> &t, DtypeKernels &k)
         make_entry<T, 128, 256, 128, 2, 2, 32, 1, 2>(d, 2, 0.4f, "bf16 128x256 k64 waves2x2 mfma32")));
     t.push_back(with_streamk<T, 128, 128, 128, 2, 2, 32, 2, 3>(
         make_entry<T, 128, 128, 128, 2, 2, 32, 0, 1, 2, 3>(d, 3, 0.4f, "bf16 128x128 k64 waves2x2 mfma32")));
+    // k-groups: WK wave groups share each chunk's k-steps (fewer LDS reads per MFMA)
+    //                    T  BM   BN   RB  waves WK MF  prefetch depths
+    t.push_back(make_entry_k<T, 128, 128, 128, 2, 1, 2, 32, 2, 3>(d, 3, 0.4f, "bf16 128x128 k64 waves2x1x2 mfma32"));
+    t.push_back(make_entry_k<T, 128, 128, 128, 1, 2, 2, 32, 2, 3>(d, 3, 0.4f, "bf16 128x128 k64 waves1x2x2 mfma32"));
+    t.push_back(make_entry_k<T, 128, 128, 128, 2, 2, 2, 32, 2, 3>(d, 3, 0.4f, "bf16 128x128 k64 waves2x2x2 mfma32"));
     t.push_back(make_entry<T, 64, 64, 128, 2, 2, 32, 1, 2, 3>(d, 2, 0.22f, "bf16 64x64 k64 waves2x2 mfma32"));
     t.push_back(make_entry<T, 128, 128, 128, 2, 2, 16, 2>(d, 2, 0.3f, "bf16 128x128 k64 waves2x2 mfma16"));
     t.push_back(make_entry<T, 256, 256, 128, 2, 2, 16, 1>(d, 1, 0.4f, "bf16 256x256 k64 waves2x2 mfma16"));
