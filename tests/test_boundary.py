@@ -207,3 +207,26 @@ def test_ctypes_struct_sizes_match_header(lib):
     # gemm_mkl_plan: 4 x int32, int64, 4 x int32, size_t, 2 x int32
     assert ctypes.sizeof(gm._binding.Opts) == 32
     assert ctypes.sizeof(gm._binding.Plan) == 56
+
+
+def test_streamk_only_where_instantiated(lib):
+    # regression: a prefetch depth beyond the launch table once spilled tile
+    # launchers into the stream-K table of a configuration; stream-K plans
+    # must exist exactly for the configurations built with stream-K kernels
+    have = set()
+    for cid, name in enumerate(gm.config_names()):
+        dt = gm.DTYPE_CODES[name.split()[0]]
+        for p in range(0, 5):
+            try:
+                plan = gm.get_plan(300, 200, 2112, 2, dt, ID, gm.make_opts(config_id=cid, prefetch_stages=p,
+                                                                             streamk=True))
+            except gm.GemmMklError as e:
+                assert e.status == -6
+                continue
+            assert plan["streamk"] == 1
+            have.add((name, p))
+    want = {("f32 64x64 k32 waves2x2 mfma32", 2),
+            ("f16 128x256 k64 waves2x2 mfma32", 2), ("bf16 128x256 k64 waves2x2 mfma32", 2),
+            ("f16 128x128 k64 waves2x2 mfma32", 2), ("f16 128x128 k64 waves2x2 mfma32", 3),
+            ("bf16 128x128 k64 waves2x2 mfma32", 2), ("bf16 128x128 k64 waves2x2 mfma32", 3)}
+    assert have == want

@@ -27,6 +27,7 @@ struct ConfigEntry {
     int mf;                // MFMA block edge (16 or 32)
     int waves_m, waves_n;  // wave grid (64 lanes each)
     int waves_k;           // wave groups splitting each chunk's k-steps
+    int producers;         // extra waves that only issue the global->LDS loads
     int default_p;         // prefetch_stages used when not forced
     float eff;             // measured fraction of the dtype's MFMA peak on large problems
     const char *name;
@@ -46,11 +47,11 @@ void register_bf16(std::vector<ConfigEntry> &table, DtypeKernels &k);
 
 // ---------------------------------------------------------------- helpers for the units
 
-template <class T, int BM, int BN, int RB, int WMW, int WNW, int MF, int P, int MODE, int WK>
+template <class T, int BM, int BN, int RB, int WMW, int WNW, int MF, int P, int MODE, int WK, int NP>
 hipError_t launch_tile(const TileParams &p, int grid, hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemm_tile_kernel<T, BM, BN, RB, WMW, WNW, MF, P, MODE, WK>), dim3(grid),
-                       dim3(WMW * WNW * WK * 64), 0, stream, p);
+    hipLaunchKernelGGL((gemm_tile_kernel<T, BM, BN, RB, WMW, WNW, MF, P, MODE, WK, NP>), dim3(grid),
+                       dim3((WMW * WNW * WK + NP) * 64), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -66,25 +67,27 @@ hipError_t launch_streamk(const StreamKParams &p, int grid, hipStream_t stream)
 template <class T, int BM, int BN, int RB, int WMW, int WNW, int MF, int P>
 void fill_streamk(ConfigEntry &e)
 {
+    static_assert(P >= 0 && P <= kMaxPrefetch, "prefetch depth outside the launch table");
     e.sk[P][MODE_IDENTITY] = &launch_streamk<T, BM, BN, RB, WMW, WNW, MF, P, MODE_IDENTITY>;
     e.sk[P][MODE_RELU] = &launch_streamk<T, BM, BN, RB, WMW, WNW, MF, P, MODE_RELU>;
     e.sk[P][MODE_SILU] = &launch_streamk<T, BM, BN, RB, WMW, WNW, MF, P, MODE_SILU>;
 }
 
-template <class T, int BM, int BN, int RB, int WMW, int WNW, int WK, int MF, int P>
+template <class T, int BM, int BN, int RB, int WMW, int WNW, int WK, int NP, int MF, int P>
 void fill_prefetch(ConfigEntry &e)
 {
-    e.fn[P][MODE_IDENTITY] = &launch_tile<T, BM, BN, RB, WMW, WNW, MF, P, MODE_IDENTITY, WK>;
-    e.fn[P][MODE_RELU] = &launch_tile<T, BM, BN, RB, WMW, WNW, MF, P, MODE_RELU, WK>;
-    e.fn[P][MODE_SILU] = &launch_tile<T, BM, BN, RB, WMW, WNW, MF, P, MODE_SILU, WK>;
-    e.fn[P][MODE_PARTIAL] = &launch_tile<T, BM, BN, RB, WMW, WNW, MF, P, MODE_PARTIAL, WK>;
+    static_assert(P >= 0 && P <= kMaxPrefetch, "prefetch depth outside the launch table");
+    e.fn[P][MODE_IDENTITY] = &launch_tile<T, BM, BN, RB, WMW, WNW, MF, P, MODE_IDENTITY, WK, NP>;
+    e.fn[P][MODE_RELU] = &launch_tile<T, BM, BN, RB, WMW, WNW, MF, P, MODE_RELU, WK, NP>;
+    e.fn[P][MODE_SILU] = &launch_tile<T, BM, BN, RB, WMW, WNW, MF, P, MODE_SILU, WK, NP>;
+    e.fn[P][MODE_PARTIAL] = &launch_tile<T, BM, BN, RB, WMW, WNW, MF, P, MODE_PARTIAL, WK, NP>;
 }
 
 // A configuration: tile BM x BN, RB bytes of K per row and chunk, a WMW x WNW
-// wave grid repeated over WK k-groups, MFMA edge MF, instantiated for
-// prefetch depths Ps.
-template <class T, int BM, int BN, int RB, int WMW, int WNW, int WK, int MF, int... Ps>
-ConfigEntry make_entry_k(int dtype, int default_p, float eff, const char *name)
+// wave grid repeated over WK k-groups plus NP producer waves, MFMA edge MF,
+// instantiated for prefetch depths Ps.
+template <class T, int BM, int BN, int RB, int WMW, int WNW, int WK, int NP, int MF, int... Ps>
+ConfigEntry make_entry_kp(int dtype, int default_p, float eff, const char *name)
 {
     ConfigEntry e{};
     e.eff = eff;
@@ -96,16 +99,23 @@ ConfigEntry make_entry_k(int dtype, int default_p, float eff, const char *name)
     e.waves_m = WMW;
     e.waves_n = WNW;
     e.waves_k = WK;
+    e.producers = NP;
     e.default_p = default_p;
     e.name = name;
-    (fill_prefetch<T, BM, BN, RB, WMW, WNW, WK, MF, Ps>(e), ...);
+    (fill_prefetch<T, BM, BN, RB, WMW, WNW, WK, NP, MF, Ps>(e), ...);
     return e;
+}
+
+template <class T, int BM, int BN, int RB, int WMW, int WNW, int WK, int MF, int... Ps>
+ConfigEntry make_entry_k(int dtype, int default_p, float eff, const char *name)
+{
+    return make_entry_kp<T, BM, BN, RB, WMW, WNW, WK, 0, MF, Ps...>(dtype, default_p, eff, name);
 }
 
 template <class T, int BM, int BN, int RB, int WMW, int WNW, int MF, int... Ps>
 ConfigEntry make_entry(int dtype, int default_p, float eff, const char *name)
 {
-    return make_entry_k<T, BM, BN, RB, WMW, WNW, 1, MF, Ps...>(dtype, default_p, eff, name);
+    return make_entry_kp<T, BM, BN, RB, WMW, WNW, 1, 0, MF, Ps...>(dtype, default_p, eff, name);
 }
 
 // Adds stream-K variants (prefetch depths Ps) to an entry made by make_entry.

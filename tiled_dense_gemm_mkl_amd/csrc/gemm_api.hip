@@ -612,7 +612,7 @@ int gemm_mkl_get_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, int
         out->block_m = c.bm;
         out->block_n = c.bn;
         out->block_k = c.rb / elem_bytes(dtype);
-        out->threads = c.waves_m * c.waves_n * c.waves_k * 64;
+        out->threads = (c.waves_m * c.waves_n * c.waves_k + c.producers) * 64;
     }
     out->workspace_bytes = plan.ws_bytes;
     out->streamk = plan.streamk ? 1 : 0;

@@ -313,12 +313,20 @@ template <class T> struct Mfma<T, 32> {
 //           so each group reads each operand fragment once; the groups' sums
 //           are added in ascending kg before the epilogue.  A chunk's LDS
 //           reads per MFMA fall by WK at the cost of one cross-wave reduction.
-template <class T, int BM, int BN, int RB, int WAVES_M, int WAVES_N, int MF, int P, int WK = 1>
+//   NP      producer waves (0: every wave loads and computes).  With NP > 0
+//           the NP extra waves issue all global->LDS loads and the MFMA waves
+//           only read LDS and compute: a direct-to-LDS load stalls the wave
+//           that issues it for many cycles when the address unit is busy,
+//           which costs a computing wave its MFMA slots but costs a producer
+//           nothing.  Needs P >= 2.
+template <class T, int BM, int BN, int RB, int WAVES_M, int WAVES_N, int MF, int P, int WK = 1, int NP = 0>
 struct TileCore {
     typedef Mfma<T, MF> MM;
     typedef typename MM::acc_t acc_t;
     static constexpr int NWT = WAVES_M * WAVES_N;        // waves of one k-group
-    static constexpr int NW = NWT * WK;
+    static constexpr int NWM = NWT * WK;                 // MFMA waves
+    static constexpr int NW = NWM + NP;
+    static constexpr int NL = NP > 0 ? NP : NW;          // waves that issue the loads
     static constexpr int THREADS = NW * 64;
     static constexpr int ES = Elem<T>::bytes;
     static constexpr int NCH = RB / 16;                  // 16-byte columns per row
@@ -335,8 +343,8 @@ struct TileCore {
     static constexpr int LDS_BYTES = SLOTS * SLOT_BYTES;
     static constexpr int A_GROUPS = BM / ROWS_PER_LOAD;
     static constexpr int B_GROUPS = BN / ROWS_PER_LOAD;
-    static constexpr int A_LOADS = A_GROUPS / NW;
-    static constexpr int B_LOADS = B_GROUPS / NW;
+    static constexpr int A_LOADS = A_GROUPS / NL;
+    static constexpr int B_LOADS = B_GROUPS / NL;
     static constexpr int LOADS = A_LOADS + B_LOADS;
     static constexpr int NMF = FM * FN;                  // MFMAs per k-step
     static constexpr int NRD = FM + FN;                  // fragment reads per k-step
@@ -365,7 +373,8 @@ struct TileCore {
     static_assert(RB == 64 || RB == 128, "row bytes");
     static_assert(MF == 16 || MF == 32, "MFMA shape");
     static_assert(BM % (MF * WAVES_M) == 0 && BN % (MF * WAVES_N) == 0, "wave tile");
-    static_assert(A_GROUPS % NW == 0 && B_GROUPS % NW == 0, "load split");
+    static_assert(A_GROUPS % NL == 0 && B_GROUPS % NL == 0, "load split");
+    static_assert(NP == 0 || P >= 2, "producer waves need a ring of at least 3 slots");
     static_assert(KSTEPS % WK == 0 && KSW >= 2 && KSW % 2 == 0,
                   "k-steps per wave and chunk: even, for the register double buffer");
     static_assert(WK == 1 || NWT * NREG * 256 <= LDS_BYTES, "LDS for the cross-group reduction");
@@ -374,7 +383,8 @@ struct TileCore {
 
     char *smem;
     uint32_t smem_base;
-    int lane, wave, wm, wn, kg, lrow, lcol, sw;
+    int lane, wave, wm, wn, kg, li, lrow, lcol, sw;
+    bool mma;   // an MFMA wave (else a producer)
     uint32_t rd_a, rd_b;
     int64_t m0, n0, k_bytes;
     int l;
@@ -390,6 +400,8 @@ struct TileCore {
         smem_base = lds_addr(lds);
         lane = threadIdx.x & 63;
         wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        mma = wave < NWM;
+        li = NP == 0 ? wave : (mma ? 0 : wave - NWM);   // loader index (producers: 0 .. NP - 1)
         kg = wave / NWT;
         wm = (wave % NWT) % WAVES_M;
         wn = (wave % NWT) / WAVES_M;
@@ -428,7 +440,7 @@ struct TileCore {
         // holding logical column that ^ swizzle(row)).
 #pragma unroll
         for (int j = 0; j < A_LOADS; ++j) {
-            const int g = wave * A_LOADS + j;
+            const int g = li * A_LOADS + j;
             const int r = g * ROWS_PER_LOAD + lane / NCH;
             const int c = (lane % NCH) ^ row_swizzle<RB>(r);
             col_a[j] = c;
@@ -436,7 +448,7 @@ struct TileCore {
         }
 #pragma unroll
         for (int j = 0; j < B_LOADS; ++j) {
-            const int g = wave * B_LOADS + j;
+            const int g = li * B_LOADS + j;
             const int r = g * ROWS_PER_LOAD + lane / NCH;
             const int c = (lane % NCH) ^ row_swizzle<RB>(r);
             col_b[j] = c;
@@ -471,14 +483,14 @@ struct TileCore {
             const int j = q;
             const uint32_t v = (col_a[j] * 16 < rem) ? voff_a[j] : kOutOfRange;
             if ((j & 3) == 0)
-                dma16_set_m0(rsrc_a, sbase + (wave * A_LOADS + j) * 1024, v, soff);
+                dma16_set_m0(rsrc_a, sbase + (li * A_LOADS + j) * 1024, v, soff);
             else
                 dma16_same_m0(rsrc_a, j & 3, v, soff);
         } else {
             const int j = q - A_LOADS;
             const uint32_t v = (col_b[j] * 16 < rem) ? voff_b[j] : kOutOfRange;
             if ((j & 3) == 0)
-                dma16_set_m0(rsrc_b, sbase + BM * RB + (wave * B_LOADS + j) * 1024, v, soff);
+                dma16_set_m0(rsrc_b, sbase + BM * RB + (li * B_LOADS + j) * 1024, v, soff);
             else
                 dma16_same_m0(rsrc_b, j & 3, v, soff);
         }
@@ -523,7 +535,7 @@ struct TileCore {
         for (int m = 0; m < NMF; ++m) {
             mfma_one(ks % NB, m);
             if (m < NRD) read_one(rslot, tks, tbuf, m);
-            if (ks < SPREAD && m % LGAP == 0 && m / LGAP < LPK) {
+            if (NP == 0 && ks < SPREAD && m % LGAP == 0 && m / LGAP < LPK) {
                 const int q = ks * LPK + m / LGAP;
                 if (q < LOADS) issue_one(load_chunk, fill, q, valid);
             }
@@ -532,7 +544,7 @@ struct TileCore {
         // reads and loads that did not fit between the MFMAs
 #pragma unroll
         for (int r = NMF; r < NRD; ++r) read_one(rslot, tks, tbuf, r);
-        if (ks < SPREAD) {
+        if (NP == 0 && ks < SPREAD) {
 #pragma unroll
             for (int u = (NMF + LGAP - 1) / LGAP; u < LPK; ++u) {
                 const int q = ks * LPK + u;
@@ -559,6 +571,41 @@ struct TileCore {
                     for (int r = 0; r < NRD; ++r) read_one(0, ks, ks & 1, r);
 #pragma unroll
                     for (int t = 0; t < NMF; ++t) mfma_one(ks & 1, t);
+                }
+            }
+        } else if constexpr (NP > 0) {
+            if (nk <= 0) return;
+            // Producer / consumer ring (same slots, chunk order and barriers as
+            // below): after the barrier that ends chunk i - 1 the producers
+            // issue chunk i + P into the slot chunk i - 1 used, wait until
+            // chunk i + 2 has landed and meet the MFMA waves at the barrier
+            // that ends chunk i.
+            if (!mma) {
+#pragma unroll
+                for (int c = 0; c < P; ++c) issue(c_begin + min(c, nk - 1), c, c < nk);
+                wait_vmcnt<LOADS * (P - 2)>();   // chunks 0 and 1 have landed
+                block_barrier();
+                int fill = P;
+                for (int i = 0; i < nk; ++i) {
+                    issue(c_begin + min(i + P, nk - 1), fill, i + P < nk);
+                    wait_vmcnt<LOADS * (P - 2)>();
+                    block_barrier();
+                    fill = (fill + 1 == SLOTS) ? 0 : fill + 1;
+                }
+                wait_vmcnt<0>();
+            } else {
+                block_barrier();
+#pragma unroll
+                for (int ks = 0; ks < RA; ++ks)
+#pragma unroll
+                    for (int r = 0; r < NRD; ++r) read_one(0, ks, ks % NB, r);
+                int slot = 0;
+                for (int i = 0; i < nk; ++i) {
+                    const int next = (slot + 1 == SLOTS) ? 0 : slot + 1;
+#pragma unroll
+                    for (int ks = 0; ks < KSW; ++ks) step(ks, slot, next, 0, 0, false);
+                    block_barrier();
+                    slot = next;
                 }
             }
         } else {
@@ -693,11 +740,11 @@ struct TileCore {
         constexpr int EPC = 16 / OES;           // elements per 16-byte column
         constexpr int RPP = THREADS / NC;       // rows per pass of the workgroup
         constexpr int GROUPS = MM::regs / 4;
-        static_assert(ROWB % 16 == 0 && THREADS % NC == 0 && BM % RPP == 0, "staged store layout");
+        static_assert(ROWB % 16 == 0 && THREADS % NC == 0, "staged store layout");
         lds_barrier();   // every wave's ring reads and loads are done
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-            if (kg != 0) break;   // (k-group 0 holds the sums)
+            if (kg != 0 || !mma) break;   // (k-group 0 holds the sums)
             const int r = wm * WTM + i * MF + lrow;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
@@ -745,7 +792,7 @@ struct TileCore {
     template <int MODE>
     __device__ __forceinline__ void store_direct(void *out, int64_t M, int64_t N)
     {
-        if (kg != 0) return;   // (k-group 0 holds the sums)
+        if (kg != 0 || !mma) return;   // (k-group 0 holds the sums)
         const bool vec_ok = (N & 3) == 0;
         constexpr int GROUPS = MM::regs / 4;
 #pragma unroll
@@ -792,7 +839,7 @@ struct TileCore {
     // so that every store and load is a coalesced 16-byte access.
     __device__ __forceinline__ void save_partial(float *W)
     {
-        static_assert(WK == 1, "stream-K pieces keep one k-group");
+        static_assert(WK == 1 && NP == 0, "stream-K pieces keep one k-group and no producers");
         const __amdgpu_buffer_rsrc_t r = partial_rsrc(W);
 #pragma unroll
         for (int q = 0; q < NREG / 4; ++q)
@@ -858,10 +905,11 @@ __device__ __forceinline__ void raster(int tile, int tiles_m, int tiles_n, int g
 }
 
 // Data-parallel / split-K grid: one workgroup per (batch, split, tile).
-template <class T, int BM, int BN, int RB, int WAVES_M, int WAVES_N, int MF, int P, int MODE, int WK = 1>
-__global__ __launch_bounds__(WAVES_M *WAVES_N *WK * 64) void gemm_tile_kernel(TileParams p)
+template <class T, int BM, int BN, int RB, int WAVES_M, int WAVES_N, int MF, int P, int MODE, int WK = 1,
+          int NP = 0>
+__global__ __launch_bounds__((WAVES_M *WAVES_N *WK + NP) * 64) void gemm_tile_kernel(TileParams p)
 {
-    typedef TileCore<T, BM, BN, RB, WAVES_M, WAVES_N, MF, P, WK> Core;
+    typedef TileCore<T, BM, BN, RB, WAVES_M, WAVES_N, MF, P, WK, NP> Core;
     __shared__ __attribute__((aligned(1024))) char smem[Core::LDS_BYTES];
     Core c;
     c.init(smem);
