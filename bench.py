@@ -178,7 +178,8 @@ def main() -> int:
     traffic = measured_traffic(key, kernel)
 
     result = {
-        "metric": "GEMM TFLOP/s + % of MFMA peak, bf16 M=512 N=5632 K=2048 ReLU, 1 MI355X",
+        "metric": ("GEMM TFLOP/s + % of MFMA peak, bf16 M=512 N=5632 K=2048 ReLU, 1 MI355X" if key == workloads.HEADLINE
+                   else f"GEMM TFLOP/s + % of MFMA peak, {w.name}, 1 MI355X"),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,

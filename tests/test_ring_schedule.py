@@ -1,0 +1,237 @@
+"""CPU model of the prefetch ring's schedule (TileCore::run in
+tiled_dense_gemm_mkl_amd/csrc/gemm_kernels.hpp), checked for the hazards a
+wrong wait count or a missing barrier would cause on the GPU.
+
+The model emits, per wave role, the program order of the ring's events: loads
+of a chunk into a slot, vmcnt waits, barriers, LDS fragment reads of
+(chunk, k-step) into a register buffer, and MFMAs.  With every wave running
+its program and meeting the others at each barrier, it checks:
+
+  RAW   every LDS read of chunk c follows a barrier that every loading wave
+        reached only after its loads of chunk c were complete (vmcnt: loads
+        complete in issue order, so `wait n` completes all but the last n);
+  WAR   every load into a slot follows a barrier that every computing wave
+        reached only after it had finished with the slot's previous chunk
+        (all MFMAs of that chunk issued, or an LDS drain at the barrier);
+  data  every MFMA consumes the fragments of its own (chunk, k-step).
+
+Planted mistakes in the schedule (a wait one too loose, a missing barrier, a
+ring slot off by one, a missing drain) must each be caught.
+"""
+
+import pytest
+
+def schedule(KSW, NMF, NRD, LOADS, P, nk, producers=False, mut=None):
+    """Per-role event lists of the ring over nk chunks (the kernel's order)."""
+    RA = 1 if (NMF >= 8 or KSW < 4) else KSW - 1
+    NB = RA + 1
+    SLOTS = P + 1
+    WIN = KSW - RA
+    SPREAD = KSW if P >= 2 else WIN
+    LPK = -(-LOADS // SPREAD)
+    WAIT = LOADS * (P - 2) if P >= 2 else 0
+    if mut == "loose_wait":
+        WAIT += 1
+    LGAP = max(1, NMF // LPK)
+    first_fill = P if mut != "slot_off" else P - 1
+
+    if not producers:
+        ev = []
+        for c in range(P):
+            for q in range(LOADS):
+                ev.append(("load", c if c < nk else None, c))
+        ev.append(("wait", LOADS * (P - 1) - (LOADS if P >= 2 else 0)))
+        ev.append(("bar", True))
+        for ks in range(RA):
+            for r in range(NRD):
+                ev.append(("read", 0, 0, ks, ks % NB))
+        slot, fill = 0, first_fill
+        for i in range(nk):
+            nxt = (slot + 1) % SLOTS
+            lc = min(i + P, nk - 1)
+            valid = i + P < nk
+            for ks in range(KSW):
+                if P == 1 and ks == WIN:
+                    ev.append(("wait", 0))
+                    ev.append(("bar", mut != "no_drain"))
+                t = ks + RA
+                in_next = t >= KSW
+                tks = t - KSW if in_next else t
+                rs, rc = (nxt, i + 1) if in_next else (slot, i)
+                for m in range(NMF):
+                    ev.append(("mfma", i, ks, ks % NB))
+                    if m < NRD:
+                        ev.append(("read", rs, rc, tks, t % NB))
+                    if ks < SPREAD and m % LGAP == 0 and m // LGAP < LPK:
+                        q = ks * LPK + m // LGAP
+                        if q < LOADS:
+                            ev.append(("load", lc if valid else None, fill))
+                for r in range(NMF, NRD):
+                    ev.append(("read", rs, rc, tks, t % NB))
+                if ks < SPREAD:
+                    for u in range(-(-NMF // LGAP), LPK):
+                        q = ks * LPK + u
+                        if q < LOADS:
+                            ev.append(("load", lc if valid else None, fill))
+            if P >= 2:
+                ev.append(("wait", WAIT))
+                if mut != "no_barrier":
+                    ev.append(("bar", False))
+            slot, fill = nxt, (fill + 1) % SLOTS
+        ev.append(("wait", 0))
+        return [ev], KSW * NMF, KSW * NRD
+
+    # producer waves load, MFMA waves read and compute
+    prod, mma = [], []
+    for c in range(P):
+        for q in range(LOADS):
+            prod.append(("load", c if c < nk else None, c))
+    prod.append(("wait", WAIT))
+    prod.append(("bar", False))
+    fill = first_fill
+    for i in range(nk):
+        for q in range(LOADS):
+            prod.append(("load", min(i + P, nk - 1) if i + P < nk else None, fill))
+        prod.append(("wait", WAIT))
+        if mut != "no_barrier":
+            prod.append(("bar", False))
+        fill = (fill + 1) % SLOTS
+    prod.append(("wait", 0))
+    mma.append(("bar", False))
+    for ks in range(RA):
+        for r in range(NRD):
+            mma.append(("read", 0, 0, ks, ks % NB))
+    slot = 0
+    for i in range(nk):
+        nxt = (slot + 1) % SLOTS
+        for ks in range(KSW):
+            t = ks + RA
+            in_next = t >= KSW
+            tks = t - KSW if in_next else t
+            rs, rc = (nxt, i + 1) if in_next else (slot, i)
+            for m in range(NMF):
+                mma.append(("mfma", i, ks, ks % NB))
+                if m < NRD:
+                    mma.append(("read", rs, rc, tks, t % NB))
+            for r in range(NMF, NRD):
+                mma.append(("read", rs, rc, tks, t % NB))
+        if mut != "no_barrier":
+            mma.append(("bar", False))
+        slot = nxt
+    return [prod, mma], KSW * NMF, KSW * NRD
+
+def check(roles, mfma_per_chunk, reads_per_chunk, LOADS, nk):
+    """Replays the roles barrier by barrier; raises AssertionError on a hazard."""
+    nbar = {sum(1 for e in ev if e[0] == "bar") for ev in roles}
+    assert len(nbar) == 1, "roles reach different numbers of barriers"
+    # per role: state at each barrier arrival
+    states = []
+    for ev in roles:
+        issued = []             # chunk of each load, in order
+        complete = set()
+        consumed = set()
+        reads = {}
+        mfmas = {}
+        at_bar = []
+        slot_of = {}            # slot -> chunk last loaded into it
+        for e in ev:
+            if e[0] == "load":
+                issued.append(e[1])
+                if e[1] is not None:
+                    slot_of[e[2]] = e[1]
+            elif e[0] == "wait":
+                lim = len(issued) - e[1]
+                for c in set(x for x in issued if x is not None):
+                    idx = [j for j, x in enumerate(issued) if x == c]
+                    if len(idx) == LOADS and all(j < lim for j in idx):
+                        complete.add(c)
+            elif e[0] == "bar":
+                if e[1]:        # lgkmcnt(0): every read issued so far has completed
+                    consumed |= {c for c, n in reads.items() if n == reads_per_chunk}
+                at_bar.append((set(complete), set(consumed), dict(slot_of)))
+            elif e[0] == "read":
+                reads[e[2]] = reads.get(e[2], 0) + 1
+            elif e[0] == "mfma":
+                mfmas[e[1]] = mfmas.get(e[1], 0) + 1
+                if mfmas[e[1]] == mfma_per_chunk:
+                    consumed.add(e[1])
+        states.append(at_bar)
+    loads_any = any(any(e[0] == "load" for e in ev) for ev in roles)
+    computes_any = [any(e[0] == "mfma" for e in ev) for ev in roles]
+    loaders = [k for k, ev in enumerate(roles) if any(e[0] == "load" for e in ev)]
+    computers = [k for k, c in enumerate(computes_any) if c]
+    assert loads_any
+    visible = [set.intersection(*(states[k][b][0] for k in loaders)) for b in range(nbar.pop())]
+    released = [set.intersection(*(states[k][b][1] for k in computers)) for b in range(len(visible))]
+    content = [{} for _ in visible]
+    for k in loaders:
+        for b in range(len(visible)):
+            content[b].update(states[k][b][2])
+    # replay each role against the barrier states
+    for ev in roles:
+        b = -1
+        writer = {}
+        regs = {}
+        for e in ev:
+            if e[0] == "bar":
+                b += 1
+            elif e[0] == "load":
+                c, s = e[1], e[2]
+                prev = writer.get(s)
+                if prev is not None and prev != c:
+                    assert b >= 0 and prev in released[b], f"WAR on slot {s}: chunk {prev} still in use"
+                if c is not None:
+                    writer[s] = c
+            elif e[0] == "read":
+                s, c, ks, buf = e[1:]
+                if c < nk:
+                    assert b >= 0 and c in visible[b], f"RAW: chunk {c} read before it landed"
+                    assert content[b].get(s) == c, f"slot {s} holds chunk {content[b].get(s)}, not {c}"
+                    if s in writer:
+                        assert writer[s] == c, f"slot {s} refilled before chunk {c} was read"
+                regs.setdefault(buf, []).append((c, ks))
+            elif e[0] == "mfma":
+                c, ks, buf = e[1:]
+                got = regs.get(buf, [])
+                assert got and got[-1] == (c, ks), f"MFMA of chunk {c} k-step {ks} got {got[-1:]}"
+    return True
+
+SHAPES = [  # (KSW, NMF, NRD, LOADS): k-steps per wave and chunk, MFMAs and reads per k-step, loads per wave
+    (4, 4, 4, 8),     # 128x128 k64, 4 waves of 64x64
+    (2, 16, 8, 8),    # 256x256 k32, 4 waves of 128x128
+    (2, 4, 4, 3),     # 128x256 k32, 8 waves
+    (4, 8, 6, 6),     # 128x256 k64, 4 waves of 64x128
+    (2, 4, 4, 4),     # k-groups: 128x128 k64, 8 waves, 2 per k-group pair
+    (8, 4, 4, 4),
+]
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("P", [1, 2, 3, 4])
+@pytest.mark.parametrize("producers", [False, True])
+def test_ring_schedule_has_no_hazard(shape, P, producers):
+    KSW, NMF, NRD, LOADS = shape
+    if producers and P < 2:
+        pytest.skip("producer waves need P >= 2")
+    if LOADS * P >= 64:
+        pytest.skip("beyond the vmcnt range")
+    for nk in (1, 2, 3, 4, 5, 7, 16):
+        roles, mpc, rpc = schedule(KSW, NMF, NRD, LOADS, P, nk, producers)
+        check(roles, mpc, rpc, LOADS, nk)
+
+@pytest.mark.parametrize("mut,producers,P", [
+    ("loose_wait", False, 3), ("loose_wait", True, 3),
+    ("no_barrier", False, 2), ("no_barrier", True, 3),
+    ("slot_off", False, 3), ("slot_off", True, 2),
+    ("no_drain", False, 1),
+])
+def test_planted_schedule_mistake_is_caught(mut, producers, P):
+    caught = False
+    for shape in SHAPES:
+        KSW, NMF, NRD, LOADS = shape
+        for nk in (3, 5, 16):
+            roles, mpc, rpc = schedule(KSW, NMF, NRD, LOADS, P, nk, producers, mut=mut)
+            try:
+                check(roles, mpc, rpc, LOADS, nk)
+            except AssertionError:
+                caught = True
+    assert caught, f"planted mistake {mut} went unnoticed"
