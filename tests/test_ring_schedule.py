@@ -21,6 +21,7 @@ ring slot off by one, a missing drain) must each be caught.
 
 import pytest
 
+
 def schedule(KSW, NMF, NRD, LOADS, P, nk, producers=False, mut=None):
     """Per-role event lists of the ring over nk chunks (the kernel's order)."""
     RA = 1 if (NMF >= 8 or KSW < 4) else KSW - 1
@@ -120,6 +121,7 @@ def schedule(KSW, NMF, NRD, LOADS, P, nk, producers=False, mut=None):
         slot = nxt
     return [prod, mma], KSW * NMF, KSW * NRD
 
+
 def check(roles, mfma_per_chunk, reads_per_chunk, LOADS, nk):
     """Replays the roles barrier by barrier; raises AssertionError on a hazard."""
     nbar = {sum(1 for e in ev if e[0] == "bar") for ev in roles}
@@ -196,6 +198,7 @@ def check(roles, mfma_per_chunk, reads_per_chunk, LOADS, nk):
                 assert got and got[-1] == (c, ks), f"MFMA of chunk {c} k-step {ks} got {got[-1:]}"
     return True
 
+
 SHAPES = [  # (KSW, NMF, NRD, LOADS): k-steps per wave and chunk, MFMAs and reads per k-step, loads per wave
     (4, 4, 4, 8),     # 128x128 k64, 4 waves of 64x64
     (2, 16, 8, 8),    # 256x256 k32, 4 waves of 128x128
@@ -204,6 +207,7 @@ SHAPES = [  # (KSW, NMF, NRD, LOADS): k-steps per wave and chunk, MFMAs and read
     (2, 4, 4, 4),     # k-groups: 128x128 k64, 8 waves, 2 per k-group pair
     (8, 4, 4, 4),
 ]
+
 
 @pytest.mark.parametrize("shape", SHAPES)
 @pytest.mark.parametrize("P", [1, 2, 3, 4])
@@ -217,6 +221,7 @@ def test_ring_schedule_has_no_hazard(shape, P, producers):
     for nk in (1, 2, 3, 4, 5, 7, 16):
         roles, mpc, rpc = schedule(KSW, NMF, NRD, LOADS, P, nk, producers)
         check(roles, mpc, rpc, LOADS, nk)
+
 
 @pytest.mark.parametrize("mut,producers,P", [
     ("loose_wait", False, 3), ("loose_wait", True, 3),
