@@ -104,6 +104,79 @@ def copy_calibration(mib: int, steps: int) -> int:
     return 0
 
 
+def bench_grouped(args, key: str) -> int:
+    """The grouped GEMM (gemm_mkl_grouped) on a grouped workload: same timing,
+    roofline and CPU-baseline conventions as the dense path."""
+    import numpy as np
+    import torch
+
+    import tiled_dense_gemm_mkl_amd as gm
+    from tiled_dense_gemm_mkl_amd import workloads
+
+    w = workloads.GROUPED_WORKLOADS[key]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    A, B, offs = workloads.make_grouped_inputs(w)
+    a = workloads.storage_to_torch(A, w.dtype).to(dev)
+    b = workloads.storage_to_torch(B, w.dtype).to(dev)
+    o = torch.from_numpy(offs).to(dev)
+    c = torch.empty((w.total_m, w.N), dtype=a.dtype, device=dev)
+    dcode, ecode = gm.DTYPE_CODES[w.dtype], gm.EPILOGUE_CODES[w.epilogue]
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    ptrs = (a.data_ptr(), b.data_ptr(), c.data_ptr(), o.data_ptr())
+
+    def step():
+        st = gm.gemm_mkl_grouped(*ptrs, w.G, w.total_m, w.N, w.K, dcode, ecode, sptr, None)
+        if st != 0:
+            raise gm.GemmMklError(st, gm.status_string(st))
+
+    for _ in range(args.warmup):
+        step()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    ev_ms = start.elapsed_time(end) / args.steps
+    peak = PEAK_TFLOPS[w.dtype]
+    value = w.flops / (ms_per_step * 1e-3) / 1e12
+    achieved = w.flops / (ev_ms * 1e-3) / 1e12
+    result = {
+        "metric": f"GEMM TFLOP/s + % of MFMA peak, {w.name}, 1 MI355X",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded; rows routed to groups by a seeded Dirichlet-multinomial)",
+        "config": {"workload": w.name, "G": w.G, "total_m": w.total_m, "N": w.N, "K": w.K,
+                   "epilogue": w.epilogue, "group_rows": np.diff(np.concatenate([[0], offs])).tolist()},
+        "pct_of_mfma_peak": round(100.0 * value / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "algorithmic_bytes": w.algorithmic_bytes, "launch_us": round(ev_ms * 1e3, 3)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        oracle.load()
+        times = []
+        while len(times) < 3:
+            t1 = time.perf_counter()
+            oracle.gemm_grouped64(A, B, offs, w.dtype, w.epilogue)
+            times.append(time.perf_counter() - t1)
+        t = sorted(times)[1]
+        result["cpu_baseline"] = {"value": round(w.flops / t / 1e12, 6), "unit": "TFLOP/s",
+                                  "cores": int(oracle.threads()), "kind": "oracle",
+                                  "sample": f"3 whole calls on the full grouped workload, median {t:.2f} s"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +201,8 @@ def main() -> int:
     from tiled_dense_gemm_mkl_amd import workloads
 
     key = args.workload or workloads.HEADLINE
+    if key in workloads.GROUPED_WORKLOADS:
+        return bench_grouped(args, key)
     w = workloads.WORKLOADS[key]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)

@@ -157,6 +157,39 @@ int gemm_mkl_ex(const void *A, const void *B, void *C,
                 const gemm_mkl_opts *opts);
 
 /*
+ * Grouped GEMM: G problems that share N and K but each have their own number
+ * of rows, as the grouped matrix product reached through framework adapters on
+ * "深入解析 CUTLASS CuTe DSL 的 JIT 函数参数生成机制" (section 5) does.  Group g
+ * owns rows [offs[g - 1], offs[g]) of A and C (offs[-1] = 0) and its own B[g]:
+ *
+ *   C[r][n] = epilogue( sum_k A[r][k] * B[g][n][k] )   for r in group g
+ *
+ * A:    device pointer, [total_m][K], K contiguous.
+ * B:    device pointer, [G][N][K], K contiguous.
+ * C:    device pointer, [total_m][N], N contiguous; rows outside every group
+ *       are left untouched.
+ * offs: DEVICE pointer to G int32 cumulative row ends (offs[G - 1] normally
+ *       equals total_m; empty groups repeat the previous end).  The kernels
+ *       read it on the GPU, so the call needs no host synchronisation; they
+ *       clamp it to a non-decreasing sequence in [0, total_m], so offsets
+ *       outside that range never address rows outside A or C.
+ * dtype, epilogue, stream: as for gemm_mkl; accumulation is fp32.
+ * opts: NULL for automatic; config_id and prefetch_stages may force a
+ *   configuration that has grouped kernels (see gemm_mkl_config_name) and its
+ *   depth; split_k > 1 or any flag is NOT_AVAILABLE (groups are never split).
+ *
+ * Returns GEMM_MKL_STATUS_OK (also for G, total_m or N equal to 0: no
+ * launch), INVALID_VALUE (negative sizes, G > 65536, total_m >= 2^31, null or
+ * element-misaligned pointers), UNSUPPORTED_DTYPE / _EPILOGUE, NOT_AVAILABLE
+ * (A or B not 16-byte aligned, K * element size not a multiple of 16, or no
+ * configuration fits) or HIP_ERROR.  Ownership as for gemm_mkl.
+ */
+int gemm_mkl_grouped(const void *A, const void *B, void *C, const int32_t *offs,
+                     int64_t G, int64_t total_m, int64_t N, int64_t K,
+                     int dtype, int epilogue, void *stream,
+                     const gemm_mkl_opts *opts);
+
+/*
  * The plan gemm_mkl_ex would execute for these arguments, without launching
  * anything: chosen configuration id, prefetch depth, split factor, grid size
  * and workspace bytes.  Returns a status like gemm_mkl_ex (argument checks

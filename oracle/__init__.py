@@ -16,6 +16,7 @@ from .oracle import (  # noqa: F401
     epilogue64,
     gemm64,
     gemm_entries64,
+    gemm_grouped64,
     gemm_rounded,
     load,
     round_to_dtype,

@@ -212,6 +212,51 @@ int oracle_gemm(const void *A, const void *B, double *C64,
 }
 
 /*
+ * Grouped GEMM (the variable-M grouped matrix product named on
+ * "深入解析 CUTLASS CuTe DSL 的 JIT 函数参数生成机制", section 5; the layout is
+ * the plainest reading): group g owns rows [offs[g - 1], offs[g]) of A
+ * ([total_m][K]) and of C64 ([total_m][N]), with offs[-1] = 0, and its own
+ * B[g] ([G][N][K]).  For every row r of group g and every n:
+ *
+ *   C64[r][n] = epilogue( sum_k A[r][k] * B[g][n][k] )
+ *
+ * with the same binary64 sum as oracle_gemm.  Rows in no group are not
+ * written.  The offsets must be non-decreasing in [0, total_m]; otherwise
+ * nothing is written and -1 is returned.
+ */
+int oracle_gemm_grouped(const void *A, const void *B, double *C64, const int32_t *offs,
+                        int64_t G, int64_t total_m, int64_t N, int64_t K,
+                        int dtype, int epilogue, int nthreads)
+{
+    int64_t prev = 0;
+    for (int64_t g = 0; g < G; ++g) {
+        if (offs[g] < prev || offs[g] > total_m)
+            return -1;
+        prev = offs[g];
+    }
+    int used = 1;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+    used = omp_get_max_threads();
+#endif
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < total_m; ++r) {
+        /* the group of row r: the first g whose end lies past r */
+        int64_t g = 0;
+        while (g < G && offs[g] <= r)
+            ++g;
+        if (g == G)
+            continue;
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = dot_row(A, B, dtype, r * K, (g * N + n) * K, K);
+            C64[r * N + n] = oracle_epilogue(acc, epilogue);
+        }
+    }
+    return used;
+}
+
+/*
  * Selected entries only: for i < count, out64[i] = C64[l[i]][m[i]][n[i]] of the
  * full GEMM above.  Used to check very large problems on sampled outputs.
  */

@@ -62,6 +62,9 @@ def _bind(lib):
                                         ctypes.c_int, ctypes.c_int,
                                         vp, vp, vp, i64, vp, ctypes.c_int]
     lib.oracle_gemm_entries.restype = ctypes.c_int
+    lib.oracle_gemm_grouped.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int]
+    lib.oracle_gemm_grouped.restype = ctypes.c_int
     lib.oracle_round.argtypes = [vp, vp, i64, ctypes.c_int]
     lib.oracle_round.restype = None
     lib.oracle_widen.argtypes = [vp, vp, i64, ctypes.c_int]
@@ -123,6 +126,25 @@ def gemm_entries64(A: np.ndarray, B: np.ndarray, dtype: str, epilogue: str,
                                         EPILOGUES[epilogue], _ptr(li), _ptr(mi), _ptr(ni),
                                         li.size, _ptr(out), nthreads)
     return out
+
+
+def gemm_grouped64(A: np.ndarray, B: np.ndarray, offs: np.ndarray, dtype: str, epilogue: str,
+                   nthreads: int = 0, lib=None) -> np.ndarray:
+    """Grouped GEMM in binary64: A [total_m, K], B [G, N, K] (stored bits), offs
+    int32 [G] cumulative row ends.  Rows in no group come back as NaN."""
+    lib = lib or load()
+    A = _check(A, dtype)
+    B = _check(B, dtype)
+    offs = np.ascontiguousarray(offs, dtype=np.int32)
+    total_m, K = A.shape
+    G, N, Kb = B.shape
+    assert Kb == K and offs.shape == (G,)
+    C = np.full((total_m, N), np.nan)
+    st = lib.oracle_gemm_grouped(_ptr(A), _ptr(B), _ptr(C), _ptr(offs), G, total_m, N, K,
+                                 DTYPES[dtype], EPILOGUES[epilogue], nthreads)
+    if st < 0:
+        raise ValueError("group offsets must be non-decreasing within [0, total_m]")
+    return C
 
 
 def round_to_dtype(y64: np.ndarray, dtype: str, lib=None) -> np.ndarray:

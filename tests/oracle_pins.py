@@ -306,6 +306,51 @@ def check_empty_K(lib):
             assert C.shape == (2, 3, 4) and np.all(C == 0.0), "K = 0 gives epilogue(0) = 0"
 
 
+def check_grouped_vs_numpy(lib):
+    """Grouped GEMM: every group's rows equal numpy's binary64 product of that
+    group's rows with its own B (within the summation error bound); integer
+    inputs exactly equal numpy's int64 product; rows in no group stay unwritten;
+    empty groups and a group of one row are covered."""
+    rng = np.random.default_rng(21)
+    for dtype in DTYPES:
+        G, N, K = 5, 37, 129
+        sizes = [3, 0, 70, 1, 0]
+        ends = np.cumsum(sizes).astype(np.int32)
+        total_m = int(ends[-1]) + 4                       # 4 trailing rows in no group
+        A = _random_bits(rng, dtype, (total_m, K))
+        B = _random_bits(rng, dtype, (G, N, K))
+        Av, Bv = _exact_values(A, dtype), _exact_values(B, dtype)
+        got = oracle.gemm_grouped64(A, B, ends, dtype, "identity", lib=lib)
+        relu = oracle.gemm_grouped64(A, B, ends, dtype, "relu", lib=lib)
+        start = 0
+        for g in range(G):
+            end = int(ends[g])
+            ref = Av[start:end] @ Bv[g].T
+            mag = np.abs(Av[start:end]) @ np.abs(Bv[g]).T
+            assert np.all(np.abs(got[start:end] - ref) <= 2 * K * 2.0 ** -53 * mag), f"group {g} ({dtype})"
+            assert np.array_equal(relu[start:end], np.maximum(got[start:end], 0.0) + 0.0)
+            start = end
+        assert np.all(np.isnan(got[start:])), "rows in no group must stay unwritten"
+        # integers: exact against numpy's int64 arithmetic, group by group
+        Ai = rng.integers(-2, 3, (total_m, K))
+        Bi = rng.integers(-2, 3, (G, N, K))
+        to_bits = {"f32": lambda x: x.astype(np.float32),
+                   "f16": lambda x: x.astype(np.float16).view(np.uint16),
+                   "bf16": lambda x: (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)}[dtype]
+        exact = oracle.gemm_grouped64(to_bits(Ai), to_bits(Bi), ends, dtype, "identity", lib=lib)
+        start = 0
+        for g in range(G):
+            end = int(ends[g])
+            assert np.array_equal(exact[start:end], (Ai[start:end] @ Bi[g].T).astype(np.float64)), f"int {g}"
+            start = end
+    # a single group covering every row is the dense GEMM of one batch
+    A = _random_bits(rng, "bf16", (9, 40))
+    B = _random_bits(rng, "bf16", (1, 6, 40))
+    one = oracle.gemm_grouped64(A, B, np.array([9], np.int32), "bf16", "silu", lib=lib)
+    dense = oracle.gemm64(A[None], B, "bf16", "silu", lib=lib)[0]
+    assert np.array_equal(one, dense)
+
+
 ALL_CHECKS = [
     check_widen_f16_exhaustive,
     check_widen_bf16_exhaustive,
@@ -319,4 +364,5 @@ ALL_CHECKS = [
     check_matmul_crosscheck,
     check_batch_and_entries,
     check_empty_K,
+    check_grouped_vs_numpy,
 ]

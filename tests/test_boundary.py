@@ -230,3 +230,41 @@ def test_streamk_only_where_instantiated(lib):
             ("f16 128x128 k64 waves2x2 mfma32", 2), ("f16 128x128 k64 waves2x2 mfma32", 3),
             ("bf16 128x128 k64 waves2x2 mfma32", 2), ("bf16 128x128 k64 waves2x2 mfma32", 3)}
     assert have == want
+
+
+@pytest.mark.parametrize("args,status", [
+    # (A, B, C, offs, G, total_m, N, K, dtype, epilogue)
+    ((FAKE, FAKE, FAKE, FAKE, 2, 8, 8, 8, 7, ID), -2),          # unknown dtype
+    ((FAKE, FAKE, FAKE, FAKE, 2, 8, 8, 8, BF16, 5), -3),        # unknown epilogue
+    ((FAKE, FAKE, FAKE, FAKE, -1, 8, 8, 8, BF16, ID), -1),      # negative sizes
+    ((FAKE, FAKE, FAKE, FAKE, 2, -8, 8, 8, BF16, ID), -1),
+    ((FAKE, FAKE, FAKE, FAKE, 2, 8, -8, 8, BF16, ID), -1),
+    ((FAKE, FAKE, FAKE, FAKE, 2, 8, 8, -8, BF16, ID), -1),
+    ((FAKE, FAKE, FAKE, FAKE, 65537, 8, 8, 8, BF16, ID), -1),  # too many groups
+    ((FAKE, FAKE, FAKE, FAKE, 2, 2 ** 31, 8, 8, BF16, ID), -1),  # rows beyond int32
+    ((FAKE, FAKE, None, FAKE, 2, 8, 8, 8, BF16, ID), -1),       # null C
+    ((FAKE, FAKE, FAKE, None, 2, 8, 8, 8, BF16, ID), -1),       # null offsets
+    ((None, FAKE, FAKE, FAKE, 2, 8, 8, 8, BF16, ID), -1),       # null A with K > 0
+    ((FAKE + 2, FAKE, FAKE, FAKE, 2, 8, 8, 8, F32, ID), -1),    # A not element-aligned
+    ((FAKE, FAKE, FAKE, FAKE + 2, 2, 8, 8, 8, BF16, ID), -1),   # offsets not int32-aligned
+    ((FAKE + 8, FAKE, FAKE, FAKE, 2, 8, 8, 8, BF16, ID), -6),   # A not 16-byte aligned
+    ((FAKE, FAKE, FAKE, FAKE, 2, 8, 8, 9, BF16, ID), -6),       # K * 2 bytes not a multiple of 16
+    ((None, None, None, None, 0, 8, 8, 8, BF16, ID), 0),        # no groups: no launch
+    ((None, None, None, None, 2, 0, 8, 8, F16, RELU), 0),       # no rows
+    ((None, None, None, None, 2, 8, 0, 8, F32, SILU), 0),       # no columns
+])
+def test_grouped_argument_checks(lib, args, status):
+    assert gm.gemm_mkl_grouped(*args, None, None) == status
+
+
+def test_grouped_option_checks(lib):
+    ok = (None, None, None, None, 0, 8, 8, 8, BF16, ID, None)
+    assert gm.gemm_mkl_grouped(*ok, gm.make_opts(split_k=2)) == -6       # groups are never split
+    o = gm.make_opts()
+    o.flags = 2
+    assert gm.gemm_mkl_grouped(*ok, o) == -6                              # no stream-K
+    assert gm.gemm_mkl_grouped(*ok, gm.make_opts(prefetch_stages=-3)) == -1
+    args = (FAKE, FAKE, FAKE, FAKE, 2, 8, 8, 64, BF16, ID, None)
+    assert gm.gemm_mkl_grouped(*args, gm.make_opts(config_id=10_000)) == -6  # no such configuration
+    f32_ids = [i for i, n in enumerate(gm.config_names()) if n.startswith("f32")]
+    assert gm.gemm_mkl_grouped(*args, gm.make_opts(config_id=f32_ids[0])) == -6  # another dtype's

@@ -1,0 +1,155 @@
+"""GPU parity of the grouped GEMM (gemm_mkl_grouped) against the CPU oracle.
+
+Group g owns rows [offs[g-1], offs[g]) of A and C and its own B[g]; rows in no
+group must be left untouched.  Random inputs meet the same tolerance as the
+dense path; integer-valued inputs are bit-exact for identity and ReLU.
+"""
+import numpy as np
+import pytest
+
+import tiled_dense_gemm_mkl_amd as gm
+from tiled_dense_gemm_mkl_amd import workloads
+from gpu_helpers import TOL, assert_bits_equal, require_gpu, tol_error, widen_bits
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ("f32", "f16", "bf16")
+SENTINEL = {"f32": np.float32(-7.0), "f16": np.uint16(0xC700), "bf16": np.uint16(0xC0E0)}   # -7 in each dtype
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _configs_of(dtype):
+    """Every configuration of dtype (those without grouped kernels answer NOT_AVAILABLE)."""
+    return [cid for cid, name in enumerate(gm.config_names()) if name.split()[0] == dtype]
+
+
+def _operands(dtype, total_m, G, N, K, seed, integer=False):
+    A, _ = workloads.random_operands(dtype, total_m, 1, K, 1, seed, integer=integer)
+    _, B = workloads.random_operands(dtype, 1, N, K, G, seed + 1, integer=integer)
+    return A[0], B
+
+
+def _run(A, B, offs, dtype, epilogue, **kw):
+    import torch
+
+    a = workloads.storage_to_torch(np.ascontiguousarray(A), dtype).cuda()
+    b = workloads.storage_to_torch(np.ascontiguousarray(B), dtype).cuda()
+    o = torch.from_numpy(np.ascontiguousarray(offs, dtype=np.int32)).cuda()
+    out_bits = np.full((A.shape[0], B.shape[1]), SENTINEL[dtype])
+    out = workloads.storage_to_torch(out_bits, dtype).cuda()
+    c = gm.gemm_grouped(a, b, o, epilogue, out=out, **kw)
+    torch.cuda.synchronize()
+    return workloads.torch_to_storage(c)
+
+
+def _check(C, ref64, A, B, dtype, K, what):
+    covered = ~np.isnan(ref64[:, 0]) if ref64.size else np.zeros(0, bool)
+    # rows in no group: untouched
+    assert np.all(C[~covered] == SENTINEL[dtype]), f"{what}: rows outside every group were written"
+    if covered.any():
+        got = widen_bits(C[covered], dtype)
+        assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+        err = tol_error(C[covered], ref64[covered], A, B, dtype, K)
+        assert err <= TOL[dtype], f"{what}: err {err:.3e} > {TOL[dtype]:.0e}"
+
+
+SIZES = [
+    [0, 5, 300, 1, 128, 0, 129, 64],      # empty groups, one row, exact and ragged tiles
+    [517],                                 # one group
+    [1] * 9,                               # many one-row groups
+]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("sizes", SIZES, ids=["mixed", "single", "ones"])
+def test_grouped_parity_all_epilogues(orc, dtype, sizes):
+    N, K = 200, 264 if dtype != "f32" else 132
+    G = len(sizes)
+    offs = np.cumsum(sizes).astype(np.int32)
+    total_m = int(offs[-1]) + 3                       # 3 trailing rows in no group
+    A, B = _operands(dtype, total_m, G, N, K, seed=77)
+    for epi in ("identity", "relu", "silu"):
+        ref = orc.gemm_grouped64(A, B, offs, dtype, epi)
+        C = _run(A, B, offs, dtype, epi)
+        _check(C, ref, A, B, dtype, K, f"{dtype} {epi} sizes={sizes}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_grouped_every_config_and_integer_bit_exact(orc, dtype):
+    sizes = [37, 0, 260, 3, 129]
+    offs = np.cumsum(sizes).astype(np.int32)
+    total_m, G, N, K = int(offs[-1]), len(sizes), 190, 512
+    A, B = _operands(dtype, total_m, G, N, K, seed=5)
+    Ai, Bi = _operands(dtype, total_m, G, N, K, seed=6, integer=True)
+    ref = orc.gemm_grouped64(A, B, offs, dtype, "relu")
+    refi = orc.round_to_dtype(orc.gemm_grouped64(Ai, Bi, offs, dtype, "identity"), dtype)
+    ran = 0
+    for cid in _configs_of(dtype):
+        try:
+            C = _run(A, B, offs, dtype, "relu", config_id=cid)
+        except gm.GemmMklError as e:
+            assert e.status == -6          # a configuration without grouped kernels
+            continue
+        ran += 1
+        _check(C, ref, A, B, dtype, K, f"config {cid}")
+        Ci = _run(Ai, Bi, offs, dtype, "identity", config_id=cid)
+        assert_bits_equal(Ci, refi, f"integer config {cid}")
+    assert ran >= 1
+
+
+def test_grouped_offsets_are_clamped(orc):
+    """Decreasing or out-of-range offsets never address rows outside A or C:
+    the kernels use the running maximum of the offsets clamped to [0, total_m]."""
+    dtype, N, K = "bf16", 96, 128
+    total_m = 200
+    raw = np.array([50, 20, 120, 400, -5, 180], np.int32)
+    A, B = _operands(dtype, total_m, len(raw), N, K, seed=9)
+    clamped = np.maximum.accumulate(np.clip(raw, 0, total_m)).astype(np.int32)
+    ref = orc.gemm_grouped64(A, B, clamped, dtype, "identity")
+    C = _run(A, B, raw, dtype, "identity")
+    _check(C, ref, A, B, dtype, K, "clamped offsets")
+
+
+def test_grouped_deterministic_and_matches_dense_for_one_group(orc):
+    import torch
+
+    dtype, M, N, K = "f16", 333, 250, 640
+    A, B = _operands(dtype, M, 1, N, K, seed=3)
+    offs = np.array([M], np.int32)
+    C1 = _run(A, B, offs, dtype, "silu")
+    C2 = _run(A, B, offs, dtype, "silu")
+    assert_bits_equal(C1, C2, "run to run")
+    ref = orc.gemm_grouped64(A, B, offs, dtype, "silu")
+    _check(C1, ref, A, B, dtype, K, "one group")
+
+
+def test_grouped_workload_parity(orc):
+    """The grouped workload bench.py times, in the launch configuration it
+    times, against the oracle on 48 sampled rows (every column of each; 16 of
+    them also with integer inputs, bit-exact)."""
+    w = workloads.GROUPED_WORKLOADS["grouped_bf16_G8_4096x5632x2048_relu"]
+    A, B, offs = workloads.make_grouped_inputs(w)
+    rows = np.random.default_rng(0).choice(w.total_m, 48, replace=False)
+    C = _run(A, B, offs, w.dtype, w.epilogue)
+    # sampled rows through the oracle (a row's group comes from the offsets)
+    groups = np.searchsorted(offs, rows, side="right")
+    for r, g in zip(rows, groups):
+        ref = orc.gemm_grouped64(A[r:r + 1], B[g:g + 1], np.array([1], np.int32), w.dtype, w.epilogue)
+        err = tol_error(C[r:r + 1], ref, A, B, w.dtype, w.K)
+        assert err <= TOL[w.dtype], f"row {r} (group {g}): err {err:.3e}"
+    Ai, Bi, _ = workloads.make_grouped_inputs(w, integer=True)
+    Ci = _run(Ai, Bi, offs, w.dtype, "relu")
+    for r, g in zip(rows[:16], groups[:16]):
+        refi = orc.round_to_dtype(orc.gemm_grouped64(Ai[r:r + 1], Bi[g:g + 1], np.array([1], np.int32),
+                                                     w.dtype, "relu"), w.dtype)
+        assert_bits_equal(Ci[r:r + 1], refi, f"integer row {r}")
+
+
+def test_grouped_empty_problems_launch_nothing():
+    for args in [(0, 8, 8, 64), (3, 0, 8, 64), (3, 8, 0, 64)]:
+        G, total_m, N, K = args
+        assert gm.gemm_mkl_grouped(None, None, None, None, G, total_m, N, K, gm.BF16, gm.EPI_RELU, None, None) == 0

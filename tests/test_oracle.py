@@ -48,6 +48,12 @@ MUTANTS = [
      "acc += widen(A, dtype, a_off + k) * widen(B, dtype, b_off + k);",
      "acc += oracle_epilogue(widen(A, dtype, a_off + k) * widen(B, dtype, b_off + k), 1);",
      ["check_bruteforce_fraction"]),
+    ("grouped: a row assigned to the next group", "while (g < G && offs[g] <= r)",
+     "while (g < G && offs[g] < r)", ["check_grouped_vs_numpy"]),
+    ("grouped: B of the wrong group", "dot_row(A, B, dtype, r * K, (g * N + n) * K, K)",
+     "dot_row(A, B, dtype, r * K, ((g > 0 ? g - 1 : 0) * N + n) * K, K)", ["check_grouped_vs_numpy"]),
+    ("grouped: rows in no group written", "        if (g == G)\n            continue;\n",
+     "        if (g == G)\n            g = G - 1;\n", ["check_grouped_vs_numpy"]),
 ]
 
 

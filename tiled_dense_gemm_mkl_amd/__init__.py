@@ -22,8 +22,10 @@ from ._binding import (  # noqa: F401
     GemmMklError,
     config_names,
     gemm,
+    gemm_grouped,
     gemm_mkl,
     gemm_mkl_ex,
+    gemm_mkl_grouped,
     get_plan,
     load,
     make_opts,

@@ -72,6 +72,7 @@ class Plan(ctypes.Structure):
 EXPORTS = (
     "gemm_mkl",
     "gemm_mkl_ex",
+    "gemm_mkl_grouped",
     "gemm_mkl_opts_init",
     "gemm_mkl_get_plan",
     "gemm_mkl_workspace_size",
@@ -100,6 +101,8 @@ def load(path: str = LIB_PATH):
     lib.gemm_mkl.restype = i32
     lib.gemm_mkl_ex.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i32, vp, ctypes.POINTER(Opts)]
     lib.gemm_mkl_ex.restype = i32
+    lib.gemm_mkl_grouped.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, vp, ctypes.POINTER(Opts)]
+    lib.gemm_mkl_grouped.restype = i32
     lib.gemm_mkl_opts_init.argtypes = [ctypes.POINTER(Opts)]
     lib.gemm_mkl_opts_init.restype = None
     lib.gemm_mkl_get_plan.argtypes = [i64, i64, i64, i64, i32, i32, ctypes.POINTER(Opts), ctypes.POINTER(Plan)]
@@ -157,6 +160,12 @@ def gemm_mkl(A_ptr, B_ptr, C_ptr, M, N, K, L, dtype, epilogue, stream=None) -> i
 def gemm_mkl_ex(A_ptr, B_ptr, C_ptr, M, N, K, L, dtype, epilogue, stream=None, opts: Opts | None = None) -> int:
     return load().gemm_mkl_ex(A_ptr, B_ptr, C_ptr, M, N, K, L, dtype, epilogue, stream,
                               ctypes.byref(opts) if opts is not None else None)
+
+
+def gemm_mkl_grouped(A_ptr, B_ptr, C_ptr, offs_ptr, G, total_m, N, K, dtype, epilogue, stream=None,
+                     opts: Opts | None = None) -> int:
+    return load().gemm_mkl_grouped(A_ptr, B_ptr, C_ptr, offs_ptr, G, total_m, N, K, dtype, epilogue, stream,
+                                   ctypes.byref(opts) if opts is not None else None)
 
 
 def get_plan(M, N, K, L, dtype, epilogue, opts: Opts | None = None) -> dict:
@@ -244,3 +253,47 @@ def gemm(a, b, epilogue: str = "identity", out=None, *, prefetch_stages=None, sp
     if st != 0:
         raise GemmMklError(st, status_string(st))
     return out3[0] if squeeze else out3
+
+
+def gemm_grouped(a, b, offs, epilogue: str = "identity", out=None, *, prefetch_stages=None, config_id=None,
+                 stream=None):
+    """Grouped GEMM on the GPU through libgemm_mkl.
+
+    a: [total_m, K]; b: [G, N, K]; offs: int32 [G] cumulative row ends of the
+    groups (on the same GPU).  Returns c [total_m, N] with the rows of group g
+    equal to epilogue(a[rows of g] @ b[g]^T); rows outside every group are left
+    as they are in `out` (uninitialised when out is None).
+    """
+    import torch
+
+    if epilogue not in EPILOGUE_CODES:
+        raise ValueError(f"unknown epilogue {epilogue!r}: expected one of {sorted(EPILOGUE_CODES)}")
+    if not all(isinstance(x, torch.Tensor) for x in (a, b, offs)):
+        raise TypeError("a, b and offs must be torch tensors")
+    if a.device.type != "cuda" or b.device != a.device or offs.device != a.device:
+        raise ValueError("a, b and offs must be on the same GPU")
+    if a.dtype != b.dtype:
+        raise TypeError(f"dtype mismatch: a is {a.dtype}, b is {b.dtype}")
+    if offs.dtype != torch.int32 or offs.dim() != 1 or not offs.is_contiguous():
+        raise TypeError("offs must be a contiguous 1-D int32 tensor")
+    if a.dim() != 2 or b.dim() != 3:
+        raise ValueError("a must be [total_m, K] and b [G, N, K]")
+    total_m, K = a.shape
+    G, N, Kb = b.shape
+    if Kb != K or offs.shape[0] != G:
+        raise ValueError(f"shape mismatch: a {tuple(a.shape)}, b {tuple(b.shape)}, offs {tuple(offs.shape)}")
+    if not (a.is_contiguous() and b.is_contiguous()):
+        raise ValueError("a and b must be contiguous (K innermost)")
+    if out is None:
+        out = torch.empty((total_m, N), dtype=a.dtype, device=a.device)
+    elif tuple(out.shape) != (total_m, N) or out.dtype != a.dtype or not out.is_contiguous() \
+            or out.device != a.device:
+        raise ValueError("out must be a contiguous [total_m, N] tensor of the operand dtype on the same GPU")
+    opts = make_opts(prefetch_stages, None, config_id)
+    s = stream if stream is not None else torch.cuda.current_stream(a.device)
+    with torch.cuda.device(a.device):
+        st = gemm_mkl_grouped(a.data_ptr(), b.data_ptr(), out.data_ptr(), offs.data_ptr(), G, total_m, N, K,
+                              _torch_dtype_code(a), EPILOGUE_CODES[epilogue], s.cuda_stream, opts)
+    if st != 0:
+        raise GemmMklError(st, status_string(st))
+    return out

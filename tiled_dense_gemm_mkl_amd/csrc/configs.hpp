@@ -16,6 +16,7 @@ constexpr int kModes = 4;         // identity, relu, silu, split-K partial
 
 typedef hipError_t (*TileLaunchFn)(const TileParams &p, int grid, hipStream_t stream);
 typedef hipError_t (*StreamKLaunchFn)(const StreamKParams &p, int grid, hipStream_t stream);
+typedef hipError_t (*GroupedLaunchFn)(const GroupedParams &p, int grid, hipStream_t stream);
 typedef hipError_t (*ReduceLaunchFn)(const float *W, void *C, int64_t total, int split, hipStream_t stream);
 typedef hipError_t (*GeneralLaunchFn)(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
                                       int64_t L, hipStream_t stream);
@@ -33,6 +34,8 @@ struct ConfigEntry {
     const char *name;
     TileLaunchFn fn[kMaxPrefetch + 1][kModes];  // null where not instantiated
     StreamKLaunchFn sk[kMaxPrefetch + 1][3];    // stream-K by epilogue, null where not instantiated
+    GroupedLaunchFn grouped[3];                 // grouped GEMM by epilogue (depth grouped_p), or null
+    int grouped_p;
 };
 
 struct DtypeKernels {
@@ -61,6 +64,27 @@ hipError_t launch_streamk(const StreamKParams &p, int grid, hipStream_t stream)
     hipLaunchKernelGGL((gemm_streamk_kernel<T, BM, BN, RB, WMW, WNW, MF, P, MODE>), dim3(grid),
                        dim3(WMW * WNW * 64), 0, stream, p);
     return hipGetLastError();
+}
+
+template <class T, int BM, int BN, int RB, int WMW, int WNW, int MF, int P, int MODE, int NP>
+hipError_t launch_grouped(const GroupedParams &p, int grid, hipStream_t stream)
+{
+    hipLaunchKernelGGL((gemm_grouped_kernel<T, BM, BN, RB, WMW, WNW, MF, P, MODE, NP>), dim3(grid),
+                       dim3((WMW * WNW + NP) * 64), 0, stream, p);
+    return hipGetLastError();
+}
+
+// Adds the grouped-GEMM kernels (prefetch depth P, NP producer waves) to an
+// entry made by make_entry_kp with the same tile and wave grid.
+template <class T, int BM, int BN, int RB, int WMW, int WNW, int NP, int MF, int P>
+ConfigEntry with_grouped(ConfigEntry e)
+{
+    static_assert(P >= 2 || NP == 0, "producer waves need a ring of at least 3 slots");
+    e.grouped[MODE_IDENTITY] = &launch_grouped<T, BM, BN, RB, WMW, WNW, MF, P, MODE_IDENTITY, NP>;
+    e.grouped[MODE_RELU] = &launch_grouped<T, BM, BN, RB, WMW, WNW, MF, P, MODE_RELU, NP>;
+    e.grouped[MODE_SILU] = &launch_grouped<T, BM, BN, RB, WMW, WNW, MF, P, MODE_SILU, NP>;
+    e.grouped_p = P;
+    return e;
 }
 
 // Stream-K variants of a configuration for prefetch depth P.

@@ -28,6 +28,7 @@ namespace {
 
 constexpr int kNumCUs = 256;          // MI355X compute units (8 XCDs x 32)
 constexpr int64_t kMaxSplit = 16;
+constexpr int64_t kMaxGroups = 65536;   // grouped GEMM: groups per call
 
 struct Registry {
     std::vector<ConfigEntry> table;
@@ -557,6 +558,81 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
     return GEMM_MKL_STATUS_OK;
 }
 
+// Grouped GEMM: checks, the configuration choice and the launch.
+int run_grouped(const void *A, const void *B, void *C, const int32_t *offs, int64_t G, int64_t total_m, int64_t N,
+                int64_t K, int dtype, int epilogue, void *stream_v, const gemm_mkl_opts *o)
+{
+    if (dtype != GEMM_MKL_F32 && dtype != GEMM_MKL_F16 && dtype != GEMM_MKL_BF16)
+        return GEMM_MKL_STATUS_UNSUPPORTED_DTYPE;
+    if (epilogue != GEMM_MKL_EPI_IDENTITY && epilogue != GEMM_MKL_EPI_RELU && epilogue != GEMM_MKL_EPI_SILU)
+        return GEMM_MKL_STATUS_UNSUPPORTED_EPILOGUE;
+    if (G < 0 || total_m < 0 || N < 0 || K < 0) return GEMM_MKL_STATUS_INVALID_VALUE;
+    if (G > kMaxGroups || total_m > INT32_MAX) return GEMM_MKL_STATUS_INVALID_VALUE;
+    const int64_t es = elem_bytes(dtype);
+    int64_t t;
+    if (!mul_ok(total_m, K, &t) || !mul_ok(t, es, &t)) return GEMM_MKL_STATUS_INVALID_VALUE;
+    if (!mul_ok(G, N, &t) || !mul_ok(t, K, &t) || !mul_ok(t, es, &t)) return GEMM_MKL_STATUS_INVALID_VALUE;
+    if (!mul_ok(total_m, N, &t) || !mul_ok(t, es, &t)) return GEMM_MKL_STATUS_INVALID_VALUE;
+    if (o) {
+        if (o->prefetch_stages < -1 || o->split_k < 0 || o->config_id < -1) return GEMM_MKL_STATUS_INVALID_VALUE;
+        if (o->flags != 0 || o->split_k > 1) return GEMM_MKL_STATUS_NOT_AVAILABLE;
+    }
+    if (G == 0 || total_m == 0 || N == 0) return GEMM_MKL_STATUS_OK;
+    if (C == nullptr || offs == nullptr) return GEMM_MKL_STATUS_INVALID_VALUE;
+    if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_MKL_STATUS_INVALID_VALUE;
+    auto al = [](const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; };
+    if (!al(A, es) || !al(B, es) || !al(C, es) || !al(offs, 4)) return GEMM_MKL_STATUS_INVALID_VALUE;
+    // the tiled kernels only: 16-byte aligned operands and rows
+    if (!al(A, 16) || !al(B, 16) || (K * es) % 16 != 0) return GEMM_MKL_STATUS_NOT_AVAILABLE;
+
+    Registry &R = registry();
+    const int forced = o ? o->config_id : -1;
+    int best = -1;
+    double best_cyc = 1e300;
+    for (int id = 0; id < (int)R.table.size(); ++id) {
+        const ConfigEntry &c = R.table[id];
+        if (c.dtype != dtype || c.grouped[epilogue] == nullptr) continue;
+        if (forced >= 0 && id != forced) continue;
+        if (o && o->prefetch_stages >= 0 && o->prefetch_stages != c.grouped_p) continue;
+        if (!fast_path_ok(c, dtype, K)) continue;
+        // every group ends in a partly filled row tile: on average half a tile each
+        const int64_t m_eff = total_m + G * c.bm / 2;
+        const double cyc = model_cycles(c, dtype, m_eff, N, K, 1, 1);
+        if (cyc < best_cyc) {
+            best_cyc = cyc;
+            best = id;
+        }
+    }
+    if (best < 0) return GEMM_MKL_STATUS_NOT_AVAILABLE;
+    const ConfigEntry &c = R.table[best];
+    GroupedParams gp;
+    gp.A = A;
+    gp.B = B;
+    gp.C = C;
+    gp.offs = offs;
+    gp.G = (int32_t)G;
+    gp.total_m = (int32_t)total_m;
+    gp.N = N;
+    gp.K = K;
+    const int64_t tiles_n = (N + c.bn - 1) / c.bn;
+    const int64_t row_tiles = (total_m + c.bm - 1) / c.bm + G;   // each group adds at most one partial tile
+    const int64_t grid = row_tiles * tiles_n;
+    if (tiles_n > INT32_MAX || row_tiles > INT32_MAX || grid > INT32_MAX) return GEMM_MKL_STATUS_NOT_AVAILABLE;
+    gp.tiles_n = (int32_t)tiles_n;
+    gp.row_tiles = (int32_t)row_tiles;
+    gp.total_chunks = (int32_t)((K * es + c.rb - 1) / c.rb);
+    if (env().log)
+        std::fprintf(stderr, "gemm_mkl_grouped: G=%lld rows=%lld N=%lld K=%lld dtype=%d epi=%d -> %s P=%d grid=%lld\n",
+                     (long long)G, (long long)total_m, (long long)N, (long long)K, dtype, epilogue, c.name,
+                     c.grouped_p, (long long)grid);
+    hipError_t e = c.grouped[epilogue](gp, (int)grid, reinterpret_cast<hipStream_t>(stream_v));
+    if (e != hipSuccess) {
+        t_last_hip = e;
+        return GEMM_MKL_STATUS_HIP_ERROR;
+    }
+    return GEMM_MKL_STATUS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -580,6 +656,12 @@ int gemm_mkl_ex(const void *A, const void *B, void *C, int64_t M, int64_t N, int
                 int epilogue, void *stream, const gemm_mkl_opts *opts)
 {
     return run(A, B, C, M, N, K, L, dtype, epilogue, stream, opts);
+}
+
+int gemm_mkl_grouped(const void *A, const void *B, void *C, const int32_t *offs, int64_t G, int64_t total_m,
+                     int64_t N, int64_t K, int dtype, int epilogue, void *stream, const gemm_mkl_opts *opts)
+{
+    return run_grouped(A, B, C, offs, G, total_m, N, K, dtype, epilogue, stream, opts);
 }
 
 int gemm_mkl_get_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, int epilogue,

@@ -938,6 +938,103 @@ __global__ __launch_bounds__((WAVES_M *WAVES_N *WK + NP) * 64) void gemm_tile_ke
         c.template store<MODE>(reinterpret_cast<T *>(p.C) + (int64_t)l * p.M * p.N, p.M, p.N);
 }
 
+// ------------------------------------------------------------------ grouped GEMM
+
+// Groups of rows over one shared K: group g owns rows [offs[g - 1], offs[g])
+// of A ([total_M][K]) and C ([total_M][N]) and its own B[g] ([N][K]):
+//   C[rows of g] = epilogue( A[rows of g] * B[g]^T )
+// (the variable-M grouped GEMM reached through torch adapters on
+// "深入解析 CUTLASS CuTe DSL 的 JIT 函数参数生成机制", section 5).
+struct GroupedParams {
+    const void *A;
+    const void *B;
+    void *C;
+    const int32_t *offs;   // device, G cumulative row ends
+    int32_t G;
+    int32_t total_m;
+    int64_t N, K;
+    int32_t tiles_n;
+    int32_t row_tiles;     // row tiles the grid covers (an upper bound on the groups' sum)
+    int32_t total_chunks;
+};
+
+// Row tile `tr` of the concatenation of every group's row tiles -> (group,
+// row tile within the group, first row, rows of the group); g = -1 past the
+// last tile.  Each wave scans the offsets 64 groups at a time (one lane per
+// group, a wave prefix sum of the tile counts), so every wave of the
+// workgroup reaches the same answer.  Offsets are clamped to a non-decreasing
+// sequence in [0, total_m], so no offsets can address rows outside A or C.
+template <int BM>
+__device__ __forceinline__ void find_group(const GroupedParams &gp, int tr, int &g, int &tm, int &row0, int &rows)
+{
+    const int lane = threadIdx.x & 63;
+    int before = 0;      // row tiles of the groups scanned so far
+    int prev_end = 0;    // clamped end of the last group scanned
+    g = -1;
+    for (int j0 = 0; j0 < gp.G; j0 += 64) {
+        const int j = j0 + lane;
+        int end = j < gp.G ? gp.offs[j] : 0;
+        // running maximum over the block (and the previous blocks): clamped ends
+        end = max(min(end, gp.total_m), 0);
+        int run = end;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int v = __shfl_up(run, d, 64);
+            if (lane >= d) run = max(run, v);
+        }
+        end = max(run, prev_end);
+        int start = __shfl_up(end, 1, 64);
+        if (lane == 0) start = prev_end;
+        const int nt = j < gp.G ? (end - start + BM - 1) / BM : 0;
+        int incl = nt;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int v = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += v;
+        }
+        const int total = __shfl(incl, 63, 64);
+        const int x = tr - before;
+        if (x < total) {
+            const unsigned long long hit = __ballot(nt > 0 && x >= incl - nt && x < incl);
+            const int src = __ffsll((long long)hit) - 1;
+            g = j0 + src;
+            tm = x - __shfl(incl - nt, src, 64);
+            row0 = __shfl(start, src, 64);
+            rows = __shfl(end - start, src, 64);
+            return;
+        }
+        before += total;
+        prev_end = __shfl(end, 63, 64);
+    }
+}
+
+template <class T, int BM, int BN, int RB, int WAVES_M, int WAVES_N, int MF, int P, int MODE, int NP>
+__global__ __launch_bounds__((WAVES_M *WAVES_N + NP) * 64) void gemm_grouped_kernel(GroupedParams gp)
+{
+    typedef TileCore<T, BM, BN, RB, WAVES_M, WAVES_N, MF, P, 1, NP> Core;
+    __shared__ __attribute__((aligned(1024))) char smem[Core::LDS_BYTES];
+    const int t = xcd_remap(blockIdx.x, gridDim.x);
+    int tr, tn;
+    raster(t, gp.row_tiles, gp.tiles_n, 4, tr, tn);
+    int g, tm, row0, rows;
+    find_group<BM>(gp, tr, g, tm, row0, rows);
+    if (g < 0) return;   // past the groups' row tiles (the same for every wave)
+    Core c;
+    c.init(smem);
+    TileParams p;
+    p.A = reinterpret_cast<const T *>(gp.A) + (int64_t)row0 * gp.K;
+    p.B = reinterpret_cast<const T *>(gp.B) + (int64_t)g * gp.N * gp.K;
+    p.C = reinterpret_cast<T *>(gp.C) + (int64_t)row0 * gp.N;
+    p.M = rows;
+    p.N = gp.N;
+    p.K = gp.K;
+    p.L = 1;
+    c.setup(p, 0, tm, (int)tn);
+    c.zero();
+    c.run(0, gp.total_chunks);
+    c.template store<MODE>(p.C, rows, gp.N);
+}
+
 // ------------------------------------------------------------------ stream-K
 
 // The (tile, chunk) units of all tiles, tile-major, are cut into gridDim.x

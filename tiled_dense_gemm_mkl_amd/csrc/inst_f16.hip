@@ -9,7 +9,8 @@ void register_f16(std::vector<ConfigEntry> &t, DtypeKernels &k)
     typedef _Float16 T;
     const int d = GEMM_MKL_F16;
     //                  T  BM   BN   RB  waves MF  prefetch depths
-    t.push_back(make_entry<T, 256, 256, 64, 2, 2, 32, 1, 2, 3, 4>(d, 4, 0.47f, "f16 256x256 k32 waves2x2 mfma32"));
+    t.push_back(with_grouped<T, 256, 256, 64, 2, 2, 0, 32, 4>(
+        make_entry<T, 256, 256, 64, 2, 2, 32, 1, 2, 3, 4>(d, 4, 0.47f, "f16 256x256 k32 waves2x2 mfma32")));
     t.push_back(make_entry<T, 256, 256, 64, 2, 4, 32, 2, 3, 4>(d, 3, 0.46f, "f16 256x256 k32 waves2x4 mfma32"));
     t.push_back(make_entry<T, 256, 256, 64, 4, 2, 32, 2, 3, 4>(d, 3, 0.46f, "f16 256x256 k32 waves4x2 mfma32"));
     t.push_back(make_entry<T, 256, 256, 128, 2, 4, 32, 1>(d, 1, 0.45f, "f16 256x256 k64 waves2x4 mfma32"));
@@ -22,7 +23,8 @@ void register_f16(std::vector<ConfigEntry> &t, DtypeKernels &k)
         make_entry<T, 128, 128, 128, 2, 2, 32, 0, 1, 2, 3>(d, 3, 0.4f, "f16 128x128 k64 waves2x2 mfma32")));
     // producer waves: NP extra waves issue every global->LDS load
     //                     T  BM   BN   RB  waves WK NP MF  prefetch depths
-    t.push_back(make_entry_kp<T, 128, 128, 128, 2, 2, 1, 4, 32, 2, 3>(d, 3, 0.42f, "f16 128x128 k64 waves2x2+4p mfma32"));
+    t.push_back(with_grouped<T, 128, 128, 128, 2, 2, 4, 32, 3>(
+        make_entry_kp<T, 128, 128, 128, 2, 2, 1, 4, 32, 2, 3>(d, 3, 0.42f, "f16 128x128 k64 waves2x2+4p mfma32")));
     t.push_back(make_entry_kp<T, 128, 128, 128, 2, 2, 1, 2, 32, 2, 3>(d, 3, 0.41f, "f16 128x128 k64 waves2x2+2p mfma32"));
     t.push_back(make_entry_kp<T, 128, 256, 128, 2, 2, 1, 4, 32, 2>(d, 2, 0.36f, "f16 128x256 k64 waves2x2+4p mfma32"));
     t.push_back(make_entry_kp<T, 256, 128, 128, 2, 2, 1, 4, 32, 2>(d, 2, 0.35f, "f16 256x128 k64 waves2x2+4p mfma32"));
@@ -32,7 +34,8 @@ void register_f16(std::vector<ConfigEntry> &t, DtypeKernels &k)
     t.push_back(make_entry_k<T, 128, 128, 128, 2, 1, 2, 32, 2, 3>(d, 3, 0.4f, "f16 128x128 k64 waves2x1x2 mfma32"));
     t.push_back(make_entry_k<T, 128, 128, 128, 1, 2, 2, 32, 2, 3>(d, 3, 0.4f, "f16 128x128 k64 waves1x2x2 mfma32"));
     t.push_back(make_entry_k<T, 128, 128, 128, 2, 2, 2, 32, 2, 3>(d, 3, 0.4f, "f16 128x128 k64 waves2x2x2 mfma32"));
-    t.push_back(make_entry<T, 64, 64, 128, 2, 2, 32, 1, 2, 3>(d, 2, 0.22f, "f16 64x64 k64 waves2x2 mfma32"));
+    t.push_back(with_grouped<T, 64, 64, 128, 2, 2, 0, 32, 2>(
+        make_entry<T, 64, 64, 128, 2, 2, 32, 1, 2, 3>(d, 2, 0.22f, "f16 64x64 k64 waves2x2 mfma32")));
     t.push_back(make_entry<T, 128, 128, 128, 2, 2, 16, 2>(d, 2, 0.3f, "f16 128x128 k64 waves2x2 mfma16"));
     t.push_back(make_entry<T, 256, 256, 128, 2, 2, 16, 1>(d, 1, 0.4f, "f16 256x256 k64 waves2x2 mfma16"));
     t.push_back(make_entry<T, 256, 256, 128, 2, 4, 16, 1>(d, 1, 0.40f, "f16 256x256 k64 waves2x4 mfma16"));

@@ -9,9 +9,10 @@ void register_f32(std::vector<ConfigEntry> &t, DtypeKernels &k)
     typedef float T;
     const int d = GEMM_MKL_F32;
     //                  T  BM   BN   RB  waves MF  prefetch depths
-    t.push_back(make_entry<T, 128, 128, 128, 2, 2, 32, 1, 2, 3>(d, 2, 0.4f, "f32 128x128 k32 waves2x2 mfma32"));
-    t.push_back(with_streamk<T, 64, 64, 128, 2, 2, 32, 2>(
-        make_entry<T, 64, 64, 128, 2, 2, 32, 0, 1, 2, 3>(d, 2, 0.4f, "f32 64x64 k32 waves2x2 mfma32")));
+    t.push_back(with_grouped<T, 128, 128, 128, 2, 2, 0, 32, 2>(
+        make_entry<T, 128, 128, 128, 2, 2, 32, 1, 2, 3>(d, 2, 0.4f, "f32 128x128 k32 waves2x2 mfma32")));
+    t.push_back(with_grouped<T, 64, 64, 128, 2, 2, 0, 32, 2>(with_streamk<T, 64, 64, 128, 2, 2, 32, 2>(
+        make_entry<T, 64, 64, 128, 2, 2, 32, 0, 1, 2, 3>(d, 2, 0.4f, "f32 64x64 k32 waves2x2 mfma32"))));
     t.push_back(make_entry<T, 64, 64, 128, 2, 2, 16, 1, 2>(d, 2, 0.38f, "f32 64x64 k32 waves2x2 mfma16"));
     t.push_back(make_entry<T, 32, 64, 128, 1, 2, 16, 1, 2, 3>(d, 2, 0.25f, "f32 32x64 k32 waves1x2 mfma16"));
     fill_dtype_kernels<T>(k);

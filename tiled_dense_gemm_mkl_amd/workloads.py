@@ -123,6 +123,61 @@ def make_inputs(w: Workload | str, integer: bool = False):
     return random_operands(w.dtype, w.M, w.N, w.K, w.L, seed, w.dist_a, w.dist_b, integer)
 
 
+@dataclass(frozen=True)
+class GroupedWorkload:
+    key: str
+    name: str
+    dtype: str
+    G: int            # groups (experts), each with its own B[g] [N][K]
+    total_m: int      # rows of A and C, routed to the groups
+    N: int
+    K: int
+    epilogue: str
+    dist_a: tuple
+    dist_b: tuple
+    seed: int
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.total_m * self.N * self.K
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        es = 4 if self.dtype == "f32" else 2
+        return es * (self.total_m * self.K + self.G * self.N * self.K + self.total_m * self.N)
+
+
+GROUPED_WORKLOADS = {
+    w.key: w
+    for w in [
+        GroupedWorkload(
+            "grouped_bf16_G8_4096x5632x2048_relu",
+            "bf16 grouped GEMM, 4096 rows routed to 8 groups (own 5632x2048 B each), ReLU",
+            "bf16", 8, 4096, 5632, 2048, "relu", ("normal", 1.0), ("normal", 0.02), 6),
+    ]
+}
+
+
+def group_sizes(G: int, total_m: int, seed: int) -> np.ndarray:
+    """Seeded uneven split of total_m rows over G groups: every row picks a
+    group with probabilities drawn from a Dirichlet(1) (so some groups are far
+    larger than others, and a group can be empty)."""
+    rng = np.random.Generator(np.random.PCG64(seed + 1000))
+    p = rng.dirichlet(np.ones(G))
+    return rng.multinomial(total_m, p).astype(np.int64)
+
+
+def make_grouped_inputs(w: GroupedWorkload | str, integer: bool = False):
+    """A [total_m, K], B [G, N, K] (stored bits) and int32 cumulative row ends."""
+    if isinstance(w, str):
+        w = GROUPED_WORKLOADS[w]
+    seed = w.seed + 100 if integer else w.seed
+    A, _ = random_operands(w.dtype, w.total_m, 1, w.K, 1, seed, w.dist_a, w.dist_b, integer)
+    _, B = random_operands(w.dtype, 1, w.N, w.K, w.G, seed + 1, w.dist_a, w.dist_b, integer)
+    offs = np.cumsum(group_sizes(w.G, w.total_m, w.seed)).astype(np.int32)
+    return A[0], B, offs
+
+
 def storage_to_torch(x: np.ndarray, dtype: str):
     """View stored bits as a torch CPU tensor of the operand dtype (no copy)."""
     import torch
