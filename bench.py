@@ -125,6 +125,7 @@ def bench_grouped(args, key: str) -> int:
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
     ptrs = (a.data_ptr(), b.data_ptr(), c.data_ptr(), o.data_ptr())
+    kernel = gm.config_names()[gm.grouped_config(w.G, w.total_m, w.N, w.K, dcode, ecode)] + " grouped"
 
     def step():
         st = gm.gemm_mkl_grouped(*ptrs, w.G, w.total_m, w.N, w.K, dcode, ecode, sptr, None)
@@ -154,10 +155,11 @@ def bench_grouped(args, key: str) -> int:
         "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic (seeded; rows routed to groups by a seeded Dirichlet-multinomial)",
         "config": {"workload": w.name, "G": w.G, "total_m": w.total_m, "N": w.N, "K": w.K,
-                   "epilogue": w.epilogue, "group_rows": np.diff(np.concatenate([[0], offs])).tolist()},
+                   "epilogue": w.epilogue, "group_rows": np.diff(np.concatenate([[0], offs])).tolist(),
+                   "kernel": kernel},
         "pct_of_mfma_peak": round(100.0 * value / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "frac": round(achieved / peak, 4), "traffic": measured_traffic(key, kernel),
                      "algorithmic_bytes": w.algorithmic_bytes, "launch_us": round(ev_ms * 1e3, 3)},
     }
     if not args.no_cpu_baseline:

@@ -189,6 +189,12 @@ int gemm_mkl_grouped(const void *A, const void *B, void *C, const int32_t *offs,
                      int dtype, int epilogue, void *stream,
                      const gemm_mkl_opts *opts);
 
+/* The configuration id gemm_mkl_grouped would use for these sizes and options
+ * (>= 0, see gemm_mkl_config_name), or a negative status: the checks of
+ * gemm_mkl_grouped that need no pointers.  Launches nothing. */
+int gemm_mkl_grouped_config(int64_t G, int64_t total_m, int64_t N, int64_t K,
+                            int dtype, int epilogue, const gemm_mkl_opts *opts);
+
 /*
  * The plan gemm_mkl_ex would execute for these arguments, without launching
  * anything: chosen configuration id, prefetch depth, split factor, grid size

@@ -268,3 +268,23 @@ def test_grouped_option_checks(lib):
     assert gm.gemm_mkl_grouped(*args, gm.make_opts(config_id=10_000)) == -6  # no such configuration
     f32_ids = [i for i, n in enumerate(gm.config_names()) if n.startswith("f32")]
     assert gm.gemm_mkl_grouped(*args, gm.make_opts(config_id=f32_ids[0])) == -6  # another dtype's
+
+
+def test_grouped_config_query(lib):
+    names = gm.config_names()
+    # a few hundred rows per group: 128-row tiles; one huge group: 256-row tiles
+    cid = gm.grouped_config(8, 4096, 5632, 2048, BF16, RELU)
+    assert names[cid].startswith("bf16 128x128")
+    cid = gm.grouped_config(1, 8192, 8192, 8192, F16, ID)
+    assert names[cid].startswith("f16 256x256")
+    cid = gm.grouped_config(4, 1000, 300, 256, F32, SILU)
+    assert names[cid].startswith("f32")
+    with pytest.raises(gm.GemmMklError) as e:
+        gm.grouped_config(4, 100, 64, 9, BF16, ID)             # K * 2 bytes not a multiple of 16
+    assert e.value.status == -6
+    with pytest.raises(gm.GemmMklError) as e:
+        gm.grouped_config(-1, 100, 64, 64, BF16, ID)
+    assert e.value.status == -1
+    with pytest.raises(gm.GemmMklError) as e:
+        gm.grouped_config(4, 100, 64, 64, 9, ID)
+    assert e.value.status == -2

@@ -27,6 +27,7 @@ from ._binding import (  # noqa: F401
     gemm_mkl_ex,
     gemm_mkl_grouped,
     get_plan,
+    grouped_config,
     load,
     make_opts,
     release_workspace,

@@ -73,6 +73,7 @@ EXPORTS = (
     "gemm_mkl",
     "gemm_mkl_ex",
     "gemm_mkl_grouped",
+    "gemm_mkl_grouped_config",
     "gemm_mkl_opts_init",
     "gemm_mkl_get_plan",
     "gemm_mkl_workspace_size",
@@ -103,6 +104,8 @@ def load(path: str = LIB_PATH):
     lib.gemm_mkl_ex.restype = i32
     lib.gemm_mkl_grouped.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, vp, ctypes.POINTER(Opts)]
     lib.gemm_mkl_grouped.restype = i32
+    lib.gemm_mkl_grouped_config.argtypes = [i64, i64, i64, i64, i32, i32, ctypes.POINTER(Opts)]
+    lib.gemm_mkl_grouped_config.restype = i32
     lib.gemm_mkl_opts_init.argtypes = [ctypes.POINTER(Opts)]
     lib.gemm_mkl_opts_init.restype = None
     lib.gemm_mkl_get_plan.argtypes = [i64, i64, i64, i64, i32, i32, ctypes.POINTER(Opts), ctypes.POINTER(Plan)]
@@ -166,6 +169,15 @@ def gemm_mkl_grouped(A_ptr, B_ptr, C_ptr, offs_ptr, G, total_m, N, K, dtype, epi
                      opts: Opts | None = None) -> int:
     return load().gemm_mkl_grouped(A_ptr, B_ptr, C_ptr, offs_ptr, G, total_m, N, K, dtype, epilogue, stream,
                                    ctypes.byref(opts) if opts is not None else None)
+
+
+def grouped_config(G, total_m, N, K, dtype, epilogue, opts: Opts | None = None) -> int:
+    """Configuration id gemm_mkl_grouped would use (raises on a negative status)."""
+    st = load().gemm_mkl_grouped_config(G, total_m, N, K, dtype, epilogue,
+                                        ctypes.byref(opts) if opts is not None else None)
+    if st < 0:
+        raise GemmMklError(st, status_string(st))
+    return st
 
 
 def get_plan(M, N, K, L, dtype, epilogue, opts: Opts | None = None) -> dict:

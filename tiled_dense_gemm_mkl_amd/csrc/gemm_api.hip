@@ -558,6 +558,35 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
     return GEMM_MKL_STATUS_OK;
 }
 
+// The configuration a grouped call uses (-1: none fits).  Sizes and options
+// are assumed checked.
+int grouped_config(int64_t G, int64_t total_m, int64_t N, int64_t K, int dtype, int epilogue,
+                   const gemm_mkl_opts *o)
+{
+    Registry &R = registry();
+    const int forced = o ? o->config_id : -1;
+    int best = -1;
+    double best_cyc = 1e300;
+    for (int id = 0; id < (int)R.table.size(); ++id) {
+        const ConfigEntry &c = R.table[id];
+        if (c.dtype != dtype || c.grouped[epilogue] == nullptr) continue;
+        if (forced >= 0 && id != forced) continue;
+        if (o && o->prefetch_stages >= 0 && o->prefetch_stages != c.grouped_p) continue;
+        if (!fast_path_ok(c, dtype, K)) continue;
+        // with several groups every group ends in a partly filled row tile;
+        // counting a whole tile per group matched the measured ranking of the
+        // tile sizes (groups of a few hundred rows run faster on 128-row than
+        // on 256-row tiles).  A single group is a plain GEMM.
+        const int64_t m_eff = G > 1 ? total_m + G * c.bm : total_m;
+        const double cyc = model_cycles(c, dtype, m_eff, N, K, 1, 1);
+        if (cyc < best_cyc) {
+            best_cyc = cyc;
+            best = id;
+        }
+    }
+    return best;
+}
+
 // Grouped GEMM: checks, the configuration choice and the launch.
 int run_grouped(const void *A, const void *B, void *C, const int32_t *offs, int64_t G, int64_t total_m, int64_t N,
                 int64_t K, int dtype, int epilogue, void *stream_v, const gemm_mkl_opts *o)
@@ -585,25 +614,9 @@ int run_grouped(const void *A, const void *B, void *C, const int32_t *offs, int6
     // the tiled kernels only: 16-byte aligned operands and rows
     if (!al(A, 16) || !al(B, 16) || (K * es) % 16 != 0) return GEMM_MKL_STATUS_NOT_AVAILABLE;
 
+    const int best = grouped_config(G, total_m, N, K, dtype, epilogue, o);
+    if (best < 0) return best == -1 ? GEMM_MKL_STATUS_NOT_AVAILABLE : best;
     Registry &R = registry();
-    const int forced = o ? o->config_id : -1;
-    int best = -1;
-    double best_cyc = 1e300;
-    for (int id = 0; id < (int)R.table.size(); ++id) {
-        const ConfigEntry &c = R.table[id];
-        if (c.dtype != dtype || c.grouped[epilogue] == nullptr) continue;
-        if (forced >= 0 && id != forced) continue;
-        if (o && o->prefetch_stages >= 0 && o->prefetch_stages != c.grouped_p) continue;
-        if (!fast_path_ok(c, dtype, K)) continue;
-        // every group ends in a partly filled row tile: on average half a tile each
-        const int64_t m_eff = total_m + G * c.bm / 2;
-        const double cyc = model_cycles(c, dtype, m_eff, N, K, 1, 1);
-        if (cyc < best_cyc) {
-            best_cyc = cyc;
-            best = id;
-        }
-    }
-    if (best < 0) return GEMM_MKL_STATUS_NOT_AVAILABLE;
     const ConfigEntry &c = R.table[best];
     GroupedParams gp;
     gp.A = A;
@@ -662,6 +675,25 @@ int gemm_mkl_grouped(const void *A, const void *B, void *C, const int32_t *offs,
                      int64_t N, int64_t K, int dtype, int epilogue, void *stream, const gemm_mkl_opts *opts)
 {
     return run_grouped(A, B, C, offs, G, total_m, N, K, dtype, epilogue, stream, opts);
+}
+
+int gemm_mkl_grouped_config(int64_t G, int64_t total_m, int64_t N, int64_t K, int dtype, int epilogue,
+                            const gemm_mkl_opts *opts)
+{
+    // the checks of gemm_mkl_grouped that need no pointers
+    if (dtype != GEMM_MKL_F32 && dtype != GEMM_MKL_F16 && dtype != GEMM_MKL_BF16)
+        return GEMM_MKL_STATUS_UNSUPPORTED_DTYPE;
+    if (epilogue != GEMM_MKL_EPI_IDENTITY && epilogue != GEMM_MKL_EPI_RELU && epilogue != GEMM_MKL_EPI_SILU)
+        return GEMM_MKL_STATUS_UNSUPPORTED_EPILOGUE;
+    if (G < 0 || total_m < 0 || N < 0 || K < 0 || G > kMaxGroups || total_m > INT32_MAX)
+        return GEMM_MKL_STATUS_INVALID_VALUE;
+    if (opts) {
+        if (opts->prefetch_stages < -1 || opts->split_k < 0 || opts->config_id < -1) return GEMM_MKL_STATUS_INVALID_VALUE;
+        if (opts->flags != 0 || opts->split_k > 1) return GEMM_MKL_STATUS_NOT_AVAILABLE;
+    }
+    if ((K * elem_bytes(dtype)) % 16 != 0) return GEMM_MKL_STATUS_NOT_AVAILABLE;
+    const int id = grouped_config(G, total_m, N, K, dtype, epilogue, opts);
+    return id >= 0 ? id : GEMM_MKL_STATUS_NOT_AVAILABLE;
 }
 
 int gemm_mkl_get_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, int epilogue,
