@@ -1,4 +1,5 @@
-"""CPU oracle for the batched "mkl" GEMM with a fused epilogue.
+"""CPU oracle for the batched "mkl" GEMM with a fused epilogue, the grouped
+GEMM, and the RMSNorm row reduction.
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline
 leg of the benchmark may import this package.  The product path (the HIP
@@ -19,6 +20,7 @@ from .oracle import (  # noqa: F401
     gemm_grouped64,
     gemm_rounded,
     load,
+    rms_norm64,
     round_to_dtype,
     threads,
     widen,

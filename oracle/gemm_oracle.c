@@ -257,6 +257,43 @@ int oracle_gemm_grouped(const void *A, const void *B, double *C64, const int32_t
 }
 
 /*
+ * RMSNorm over the last axis (the worked example of "一个可定制的编译器，用于为
+ * AI模型生成高效的融合GPU内核": torch.nn.RMSNorm over rows of hidden size H,
+ * whose loop nest squares and sums a row, scales the sum by 1/H, adds eps,
+ * takes the reciprocal square root, and multiplies each element by it and by
+ * the weight).  For every row r and column j of x ([rows][H]):
+ *
+ *   ms  = (sum_{j'} x[r][j']^2) / H
+ *   y64[r][j] = (x[r][j] * (1 / sqrt(ms + eps))) * w[j]
+ *
+ * all in binary64 (squares summed in ascending j from +0.0), left unrounded:
+ * oracle_round rounds the result once to the output type.  eps is taken as
+ * given (the caller passes the value the GPU adds).
+ */
+int oracle_rms_norm(const void *x, const void *w, double *y64, int64_t rows, int64_t H,
+                    double eps, int dtype, int nthreads)
+{
+    int used = 1;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+    used = omp_get_max_threads();
+#endif
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        double ss = 0.0;
+        for (int64_t j = 0; j < H; ++j) {
+            double v = widen(x, dtype, r * H + j);
+            ss += v * v;
+        }
+        double inv = 1.0 / sqrt(ss / (double)H + eps);
+        for (int64_t j = 0; j < H; ++j)
+            y64[r * H + j] = (widen(x, dtype, r * H + j) * inv) * widen(w, dtype, j);
+    }
+    return used;
+}
+
+/*
  * Selected entries only: for i < count, out64[i] = C64[l[i]][m[i]][n[i]] of the
  * full GEMM above.  Used to check very large problems on sampled outputs.
  */

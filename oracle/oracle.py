@@ -65,6 +65,8 @@ def _bind(lib):
     lib.oracle_gemm_grouped.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_int]
     lib.oracle_gemm_grouped.restype = ctypes.c_int
+    lib.oracle_rms_norm.argtypes = [vp, vp, vp, i64, i64, ctypes.c_double, ctypes.c_int, ctypes.c_int]
+    lib.oracle_rms_norm.restype = ctypes.c_int
     lib.oracle_round.argtypes = [vp, vp, i64, ctypes.c_int]
     lib.oracle_round.restype = None
     lib.oracle_widen.argtypes = [vp, vp, i64, ctypes.c_int]
@@ -145,6 +147,21 @@ def gemm_grouped64(A: np.ndarray, B: np.ndarray, offs: np.ndarray, dtype: str, e
     if st < 0:
         raise ValueError("group offsets must be non-decreasing within [0, total_m]")
     return C
+
+
+def rms_norm64(x: np.ndarray, w: np.ndarray, eps: float, dtype: str,
+               nthreads: int = 0, lib=None) -> np.ndarray:
+    """RMSNorm of the rows of x ([rows, H], stored bits) with weight w ([H]) in
+    binary64, unrounded.  eps is used as given."""
+    x = _check(x, dtype)
+    w = _check(w, dtype)
+    rows, H = x.shape
+    if w.shape != (H,):
+        raise ValueError(f"weight shape {w.shape} does not match hidden size {H}")
+    y = np.empty((rows, H), dtype=np.float64)
+    (lib or load()).oracle_rms_norm(_ptr(x), _ptr(w), _ptr(y), rows, H, float(eps),
+                                    DTYPES[dtype], nthreads)
+    return y
 
 
 def round_to_dtype(y64: np.ndarray, dtype: str, lib=None) -> np.ndarray:

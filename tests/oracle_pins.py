@@ -6,7 +6,8 @@ AssertionError when the oracle disagrees with:
   - closed forms (identity B gives C = epilogue(A); all-ones gives C = K),
   - numpy's binary64 matmul and conversions, torch's exact bf16 widening,
   - the IEEE round-to-nearest-even definition at constructed midpoints,
-  - high-precision SiLU from mpmath.
+  - high-precision SiLU and RMSNorm from mpmath, torch's own binary64 RMSNorm,
+    closed forms and invariants of the RMSNorm.
 
 The functions are shared by ``test_oracle.py`` (they must pass on the real
 oracle) and by the planted-mistake test (each mutant must fail one of them).
@@ -351,6 +352,96 @@ def check_grouped_vs_numpy(lib):
     assert np.array_equal(one, dense)
 
 
+# ------------------------------------------------------------------ RMSNorm
+
+def _rms_mp(xv, wv, eps):
+    """RMSNorm of one row at 200 bits: x_j * w_j / sqrt(mean(x^2) + eps)."""
+    import mpmath
+
+    mpmath.mp.prec = 200
+    xs = [mpmath.mpf(float(v)) for v in xv]
+    ms = mpmath.fsum(v * v for v in xs) / len(xs)
+    inv = 1 / mpmath.sqrt(ms + mpmath.mpf(float(eps)))
+    return np.array([float(v * inv * mpmath.mpf(float(w))) for v, w in zip(xs, wv)])
+
+
+def check_rms_norm_vs_torch_and_mp(lib):
+    """RMSNorm agrees with torch.nn.functional.rms_norm run in binary64 on the
+    exact input values (an implementation of its own) and, on short rows, with
+    a 200-bit evaluation of the definition, for every dtype, ragged hidden
+    sizes and random weights."""
+    import torch
+    import torch.nn.functional as F
+
+    rng = np.random.default_rng(31)
+    for dtype in DTYPES:
+        for rows, H, eps in [(5, 2048, 1e-6), (3, 37, 1e-5), (4, 1, 1e-6), (2, 3584, 0.0)]:
+            x = _random_bits(rng, dtype, (rows, H), scale=3.0)
+            w = _random_bits(rng, dtype, (H,))
+            xv, wv = _exact_values(x, dtype), _exact_values(w, dtype)
+            got = oracle.rms_norm64(x, w, eps, dtype, lib=lib)
+            ref = F.rms_norm(torch.from_numpy(xv), (H,), weight=torch.from_numpy(wv), eps=eps).numpy()
+            scale = np.abs(xv * wv) / np.sqrt((xv * xv).mean(axis=1, keepdims=True) + eps)
+            assert np.all(np.abs(got - ref) <= 1e-12 * scale + 1e-300), f"vs torch ({dtype}, H={H})"
+            if H <= 64:
+                for r in range(rows):
+                    mp = _rms_mp(xv[r], wv, eps)
+                    assert np.all(np.abs(got[r] - mp) <= 4 * 2.0 ** -52 * scale[r] + 1e-300), f"vs mp ({dtype})"
+
+
+def check_rms_norm_closed_forms(lib):
+    """Closed forms: a constant row c with unit weight gives c / sqrt(c^2 + eps);
+    with eps = 0 and c a power of two it gives exactly +-1; a zero row gives 0
+    (eps keeps the reciprocal finite); a row much smaller than sqrt(eps) is
+    scaled by about 1/sqrt(eps), since eps sits inside the square root."""
+    def const(dtype, shape, v):     # v is exactly representable in every dtype used here
+        if dtype == "f32":
+            return np.full(shape, v, np.float32)
+        if dtype == "f16":
+            return np.full(shape, v, np.float16).view(np.uint16)
+        return (np.full(shape, v, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+    for dtype in DTYPES:
+        H = 64
+        w = const(dtype, (H,), 1.0)
+        for c, eps in [(2.0, 0.0), (-0.5, 0.0), (0.75, 1e-6), (3.0, 0.25)]:
+            x = const(dtype, (1, H), c)
+            got = oracle.rms_norm64(x, w, eps, dtype, lib=lib)
+            want = c / math.sqrt(c * c + eps)
+            assert np.all(np.abs(got - want) <= 2 * 2.0 ** -52 * abs(want)), f"constant row {c} ({dtype})"
+            if eps == 0.0:
+                assert np.all(got == math.copysign(1.0, c)), "power-of-two row must normalise exactly"
+        zero = np.zeros((2, H), np.float32 if dtype == "f32" else np.uint16)
+        got = oracle.rms_norm64(zero, w, 1e-6, dtype, lib=lib)
+        assert np.all(got == 0.0), "zero row"
+    # tiny row in fp32: x = 2^-20 everywhere, eps = 1e-6  ->  y = x / sqrt(x^2 + eps)
+    H = 16
+    x = np.full((1, H), 2.0 ** -20, np.float32)
+    got = oracle.rms_norm64(x, np.ones(H, np.float32), 1e-6, "f32", lib=lib)
+    want = 2.0 ** -20 / math.sqrt(2.0 ** -40 + 1e-6)
+    assert abs(got[0, 0] - want) <= 4 * 2.0 ** -52 * want, "eps belongs inside the square root"
+
+
+def check_rms_norm_invariants(lib):
+    """Rows are independent (permuting rows permutes the result bitwise); with
+    eps = 0 scaling a row by a power of two leaves it unchanged bitwise and the
+    normalised row (unit weight) has mean square 1; the weight scales each
+    column (result with weight w == result with unit weight times w)."""
+    rng = np.random.default_rng(32)
+    rows, H = 6, 300
+    x = rng.standard_normal((rows, H)).astype(np.float32)
+    w = rng.standard_normal(H).astype(np.float32)
+    ones = np.ones(H, np.float32)
+    base = oracle.rms_norm64(x, w, 1e-6, "f32", lib=lib)
+    perm = rng.permutation(rows)
+    assert np.array_equal(oracle.rms_norm64(x[perm], w, 1e-6, "f32", lib=lib), base[perm]), "rows"
+    n0 = oracle.rms_norm64(x, ones, 0.0, "f32", lib=lib)
+    assert np.array_equal(oracle.rms_norm64(x * np.float32(8.0), ones, 0.0, "f32", lib=lib), n0), "scale"
+    assert np.all(np.abs((n0 * n0).mean(axis=1) - 1.0) <= 1e-13), "mean square of a normalised row"
+    unit = oracle.rms_norm64(x, ones, 1e-6, "f32", lib=lib)
+    assert np.array_equal(unit * w.astype(np.float64), base), "weight per column"
+
+
 ALL_CHECKS = [
     check_widen_f16_exhaustive,
     check_widen_bf16_exhaustive,
@@ -365,4 +456,7 @@ ALL_CHECKS = [
     check_batch_and_entries,
     check_empty_K,
     check_grouped_vs_numpy,
+    check_rms_norm_vs_torch_and_mp,
+    check_rms_norm_closed_forms,
+    check_rms_norm_invariants,
 ]

@@ -54,6 +54,16 @@ MUTANTS = [
      "dot_row(A, B, dtype, r * K, ((g > 0 ? g - 1 : 0) * N + n) * K, K)", ["check_grouped_vs_numpy"]),
     ("grouped: rows in no group written", "        if (g == G)\n            continue;\n",
      "        if (g == G)\n            g = G - 1;\n", ["check_grouped_vs_numpy"]),
+    ("RMSNorm: mean over H - 1 entries", "sqrt(ss / (double)H + eps)", "sqrt(ss / (double)(H - 1) + eps)",
+     ["check_rms_norm_vs_torch_and_mp", "check_rms_norm_invariants"]),
+    ("RMSNorm: eps outside the square root", "1.0 / sqrt(ss / (double)H + eps)",
+     "1.0 / (sqrt(ss / (double)H) + eps)", ["check_rms_norm_closed_forms"]),
+    ("RMSNorm: weight indexed by row", "* widen(w, dtype, j)", "* widen(w, dtype, r)",
+     ["check_rms_norm_vs_torch_and_mp", "check_rms_norm_invariants"]),
+    ("RMSNorm: first square dropped", "for (int64_t j = 0; j < H; ++j) {\n            double v",
+     "for (int64_t j = 1; j < H; ++j) {\n            double v", ["check_rms_norm_vs_torch_and_mp"]),
+    ("RMSNorm: rows share the first row's sum", "widen(x, dtype, r * H + j);\n            ss",
+     "widen(x, dtype, j);\n            ss", ["check_rms_norm_vs_torch_and_mp", "check_rms_norm_invariants"]),
 ]
 
 
