@@ -3,6 +3,9 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload KEY]
 
+(--workload takes a GEMM, grouped GEMM or RMSNorm workload key; the default is
+the headline GEMM.)
+
 A step is one call of the C entry point gemm_mkl on the headline workload
 (bf16 GEMM M=512 N=5632 K=2048 L=1, ReLU epilogue), i.e. one pass of the whole
 path (tiling, LDS-staged prefetch ring, MFMA mainloop, fused epilogue; plus the
@@ -35,15 +38,18 @@ KERNEL_SOURCES = ["tiled_dense_gemm_mkl_amd/csrc/gemm_kernels.hpp",
                   "tiled_dense_gemm_mkl_amd/csrc/inst_f32.hip"]
 
 
-def source_hash() -> str:
+RMS_KERNEL_SOURCES = ["tiled_dense_gemm_mkl_amd/csrc/rms_norm.hip"]
+
+
+def source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload_key: str, kernel: str):
+def measured_traffic(workload_key: str, kernel: str, sources=None):
     """HBM bytes per launch from the committed rocprofv3 counter readings
     (FETCH_SIZE and WRITE_SIZE, scaled by the copy-kernel calibration), if they
     were taken on the current device code and the same kernel (else None)."""
@@ -54,7 +60,7 @@ def measured_traffic(workload_key: str, kernel: str):
         with open(path) as f:
             d = json.load(f)
         e = d.get("workloads", {}).get(workload_key)
-        if not e or e.get("source_hash") != source_hash() or e.get("kernel") != kernel:
+        if not e or e.get("source_hash") != source_hash(sources) or e.get("kernel") != kernel:
             return None
         return int(e["bytes_per_launch"])
     except (OSError, ValueError, KeyError, TypeError):
@@ -179,6 +185,89 @@ def bench_grouped(args, key: str) -> int:
     return 0
 
 
+def bench_rms_norm(args, key: str) -> int:
+    """RMSNorm (gemm_mkl_rms_norm) on an RMSNorm workload.  A step is one call
+    over all rows; the kernel streams x once and writes y once, so it is
+    HBM-bound and its roofline is HBM bandwidth."""
+    import torch
+
+    import tiled_dense_gemm_mkl_amd as gm
+    from tiled_dense_gemm_mkl_amd import workloads
+
+    w = workloads.RMSNORM_WORKLOADS[key]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    X, W = workloads.make_rms_inputs(w)
+    x = workloads.storage_to_torch(X, w.dtype).to(dev)
+    wt = workloads.storage_to_torch(W, w.dtype).to(dev)
+    y = torch.empty_like(x)
+    dcode = gm.DTYPE_CODES[w.dtype]
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    xp, wp, yp = x.data_ptr(), wt.data_ptr(), y.data_ptr()
+    variant = gm.rms_norm_variant(w.rows, w.hidden, dcode, True)
+    kernel = "rms_norm " + gm.rms_norm_variant_names()[variant]
+
+    def step():
+        st = gm.gemm_mkl_rms_norm(xp, wp, yp, w.rows, w.hidden, w.eps, dcode, sptr)
+        if st != 0:
+            raise gm.GemmMklError(st, gm.status_string(st))
+
+    for _ in range(args.warmup):
+        step()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    ev_ms = start.elapsed_time(end) / args.steps
+    nbytes = w.algorithmic_bytes
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (ev_ms * 1e-3) / 1e9
+    result = {
+        "metric": f"RMSNorm GB/s (x read + y written + weight), {w.name}, 1 MI355X",
+        "value": round(value, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded; x ~ N(0,1))",
+        "config": {"workload": w.name, "rows": w.rows, "hidden": w.hidden, "eps": w.eps, "kernel": kernel},
+        "us_per_call": round(ms_per_step * 1e3, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_GBS, 4),
+                     "traffic": measured_traffic(key, kernel, RMS_KERNEL_SOURCES),
+                     "algorithmic_bytes": nbytes, "launch_us": round(ev_ms * 1e3, 3)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        oracle.load()
+        # a bounded prefix of the rows (the same rows the GPU normalises first),
+        # repeated until about 10 s of CPU work
+        rows = min(w.rows, 8192)
+        Xs, _ = workloads.make_rms_inputs(w, rows=rows)
+        times, t_total = [], 0.0
+        while t_total < 10.0 or len(times) < 3:
+            t1 = time.perf_counter()
+            oracle.rms_norm64(Xs, W, w.eps, w.dtype)
+            dt = time.perf_counter() - t1
+            times.append(dt)
+            t_total += dt
+        t = sorted(times)[len(times) // 2]
+        es = 4 if w.dtype == "f32" else 2
+        sample_bytes = es * (2 * rows * w.hidden + w.hidden)
+        result["cpu_baseline"] = {"value": round(sample_bytes / t / 1e9, 6), "unit": "GB/s",
+                                  "cores": int(oracle.threads()), "kind": "oracle",
+                                  "sample": f"{len(times)} calls on the first {rows} rows of the workload, "
+                                            f"binary64, median {t * 1e3:.3f} ms per call"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,6 +294,8 @@ def main() -> int:
     key = args.workload or workloads.HEADLINE
     if key in workloads.GROUPED_WORKLOADS:
         return bench_grouped(args, key)
+    if key in workloads.RMSNORM_WORKLOADS:
+        return bench_rms_norm(args, key)
     w = workloads.WORKLOADS[key]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)

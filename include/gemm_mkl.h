@@ -189,6 +189,53 @@ int gemm_mkl_grouped(const void *A, const void *B, void *C, const int32_t *offs,
                      int dtype, int epilogue, void *stream,
                      const gemm_mkl_opts *opts);
 
+/*
+ * RMSNorm over the last axis, the row reduction that "一个可定制的编译器，用于为
+ * AI模型生成高效的融合GPU内核" lowers from torch.nn.RMSNorm (its Loop IR and
+ * generated kernel): for every row r and column j
+ *
+ *   y[r][j] = (x[r][j] * rsqrt(sum_j' x[r][j']^2 * (1/hidden) + eps)) * weight[j]
+ *
+ * x:      device pointer, [rows][hidden], hidden contiguous.
+ * weight: device pointer to hidden elements, or NULL for no weight (y = x * rsqrt(...)).
+ * y:      device pointer, [rows][hidden]; may equal x (in place); any other
+ *         overlap with x or weight is undefined.
+ * x, weight and y share dtype (GEMM_MKL_F32/F16/BF16); the sum, rsqrt and
+ * products run in fp32 and the result is rounded once (round to nearest even)
+ * to the dtype.  eps must be finite and >= 0.  The squares are summed in an
+ * order fixed by hidden and the kernel variant: results are bitwise
+ * reproducible.
+ *
+ * Returns GEMM_MKL_STATUS_OK (also for rows or hidden equal to 0: no launch),
+ * INVALID_VALUE (negative sizes, hidden >= 2^31, size overflow, eps negative,
+ * NaN or infinite, null x or y for a non-empty problem, element-misaligned
+ * pointers), UNSUPPORTED_DTYPE or HIP_ERROR.  Enqueued on `stream` (a
+ * hipStream_t, NULL = default stream); nothing is allocated and the call does
+ * not synchronise.
+ */
+int gemm_mkl_rms_norm(const void *x, const void *weight, void *y,
+                      int64_t rows, int64_t hidden, float eps,
+                      int dtype, void *stream);
+
+/* gemm_mkl_rms_norm with a forced kernel variant (-1 = automatic; see
+ * gemm_mkl_rms_norm_variant_name).  Variant 0 is the general kernel (any
+ * hidden, element-aligned pointers); the others are vector kernels that need
+ * 16-byte aligned x, weight and y, hidden * element size a multiple of 16 and
+ * a row no longer than the variant covers: otherwise NOT_AVAILABLE.  A
+ * variant outside [-1, gemm_mkl_rms_norm_num_variants()) is INVALID_VALUE. */
+int gemm_mkl_rms_norm_ex(const void *x, const void *weight, void *y,
+                         int64_t rows, int64_t hidden, float eps,
+                         int dtype, void *stream, int variant);
+
+/* The variant gemm_mkl_rms_norm would use for these sizes, given whether x,
+ * weight and y are all 16-byte aligned (aligned != 0).  Launches nothing;
+ * returns a variant id >= 0 or a negative status. */
+int gemm_mkl_rms_norm_variant(int64_t rows, int64_t hidden, int dtype, int aligned);
+
+/* Number of RMSNorm kernel variants, and the name of one (NULL when out of range). */
+int gemm_mkl_rms_norm_num_variants(void);
+const char *gemm_mkl_rms_norm_variant_name(int variant);
+
 /* The configuration id gemm_mkl_grouped would use for these sizes and options
  * (>= 0, see gemm_mkl_config_name), or a negative status: the checks of
  * gemm_mkl_grouped that need no pointers.  Launches nothing. */

@@ -288,3 +288,56 @@ def test_grouped_config_query(lib):
     with pytest.raises(gm.GemmMklError) as e:
         gm.grouped_config(4, 100, 64, 64, 9, ID)
     assert e.value.status == -2
+
+
+# ------------------------------------------------------------------ RMSNorm
+
+@pytest.mark.parametrize("args,status", [
+    # (x, weight, y, rows, hidden, eps, dtype, variant)
+    ((FAKE, FAKE, FAKE, 4, 64, 1e-6, 7, -1), -2),                   # unknown dtype
+    ((FAKE, FAKE, FAKE, -1, 64, 1e-6, F32, -1), -1),                # negative sizes
+    ((FAKE, FAKE, FAKE, 4, -64, 1e-6, F32, -1), -1),
+    ((FAKE, FAKE, FAKE, 4, 2 ** 31, 1e-6, BF16, -1), -1),           # hidden beyond int32
+    ((FAKE, FAKE, FAKE, 2 ** 62, 2 ** 20, 1e-6, F32, -1), -1),      # size overflow
+    ((FAKE, FAKE, FAKE, 4, 64, -1e-6, F32, -1), -1),                # eps < 0
+    ((FAKE, FAKE, FAKE, 4, 64, float("nan"), F32, -1), -1),         # eps NaN
+    ((FAKE, FAKE, FAKE, 4, 64, float("inf"), F32, -1), -1),         # eps infinite
+    ((None, FAKE, FAKE, 4, 64, 1e-6, F32, -1), -1),                 # null x
+    ((FAKE, FAKE, None, 4, 64, 1e-6, F32, -1), -1),                 # null y
+    ((FAKE + 2, FAKE, FAKE, 4, 64, 1e-6, F32, -1), -1),             # x not element-aligned
+    ((FAKE, FAKE + 1, FAKE, 4, 64, 1e-6, BF16, -1), -1),            # weight not element-aligned
+    ((FAKE, FAKE, FAKE, 4, 64, 1e-6, F32, 99), -1),                 # no such variant
+    ((FAKE, FAKE, FAKE, 4, 64, 1e-6, F32, -2), -1),
+    ((FAKE + 4, FAKE, FAKE, 4, 64, 1e-6, F32, 1), -6),              # vector variant, x not 16-byte aligned
+    ((FAKE, FAKE, FAKE, 4, 3, 1e-6, F32, 1), -6),                   # vector variant, row not 16-byte multiple
+    ((FAKE, FAKE, FAKE, 4, 512, 1e-6, F32, 1), -6),                 # vector variant covering 256 floats
+    ((None, None, None, 0, 64, 1e-6, F32, -1), 0),                  # no rows: no launch
+    ((None, None, None, 4, 0, 1e-6, BF16, -1), 0),                  # no columns
+])
+def test_rms_norm_argument_checks(lib, args, status):
+    x, w, y, rows, hidden, eps, dtype, variant = args
+    assert gm.gemm_mkl_rms_norm(x, w, y, rows, hidden, eps, dtype, None, variant) == status
+
+
+def test_rms_norm_plain_entry_matches_ex_checks(lib):
+    assert lib.gemm_mkl_rms_norm(None, None, None, 0, 8, 1e-6, F32, None) == 0
+    assert lib.gemm_mkl_rms_norm(FAKE, FAKE, FAKE, 4, 64, -1.0, F32, None) == -1
+    assert lib.gemm_mkl_rms_norm(FAKE, FAKE, FAKE, 4, 64, 1e-6, 3, None) == -2
+
+
+def test_rms_norm_variant_choice(lib):
+    names = gm.rms_norm_variant_names()
+    assert names[0] == "general" and len(names) == lib.gemm_mkl_rms_norm_num_variants()
+    assert lib.gemm_mkl_rms_norm_variant_name(len(names)) is None
+    pick = lambda rows, h, dt, al=True: names[gm.rms_norm_variant(rows, h, dt, al)]
+    assert pick(32, 2048, F32) == "vec nv1 w8"          # one vector of 4 floats per lane, 8 waves
+    assert pick(32, 2048, BF16) == "vec nv4 w1"
+    assert pick(32, 3584, BF16) == "vec nv1 w8"         # a partly filled last vector step
+    assert pick(32, 8192, BF16) == "vec nv4 w4"
+    assert pick(32, 256, F16) == "vec nv1 w1"
+    assert pick(4, 32768, F32) == "vec nv8 w16"         # the longest vector row
+    assert pick(4, 32772, F32) == "general"             # beyond every vector variant
+    assert pick(4, 3, F32) == "general"                 # 12-byte rows
+    assert pick(4, 2048, F32, False) == "general"       # unaligned pointers
+    with pytest.raises(gm.GemmMklError):
+        gm.rms_norm_variant(4, 64, 9)

@@ -2,7 +2,8 @@
 
     C[l][m][n] = epilogue( sum_k A[l][m][k] * B[l][n][k] )
 
-The computation runs in hand-written gfx950 HIP kernels behind the C ABI of
+A second kernel normalises rows (RMSNorm, ``rms_norm``).  The computation
+runs in hand-written gfx950 HIP kernels behind the C ABI of
 ``include/gemm_mkl.h`` (``lib/libgemm_mkl.so``); this package is the thin
 Python binding (argument marshalling only).  PyTorch supplies device memory
 and streams.
@@ -26,11 +27,15 @@ from ._binding import (  # noqa: F401
     gemm_mkl,
     gemm_mkl_ex,
     gemm_mkl_grouped,
+    gemm_mkl_rms_norm,
     get_plan,
     grouped_config,
     load,
     make_opts,
     release_workspace,
+    rms_norm,
+    rms_norm_variant,
+    rms_norm_variant_names,
     status_string,
     workspace_size,
 )

@@ -82,6 +82,11 @@ EXPORTS = (
     "gemm_mkl_num_configs",
     "gemm_mkl_config_name",
     "gemm_mkl_version",
+    "gemm_mkl_rms_norm",
+    "gemm_mkl_rms_norm_ex",
+    "gemm_mkl_rms_norm_variant",
+    "gemm_mkl_rms_norm_num_variants",
+    "gemm_mkl_rms_norm_variant_name",
 )
 
 _lib = None
@@ -122,6 +127,16 @@ def load(path: str = LIB_PATH):
     lib.gemm_mkl_config_name.restype = ctypes.c_char_p
     lib.gemm_mkl_version.argtypes = []
     lib.gemm_mkl_version.restype = i32
+    lib.gemm_mkl_rms_norm.argtypes = [vp, vp, vp, i64, i64, ctypes.c_float, i32, vp]
+    lib.gemm_mkl_rms_norm.restype = i32
+    lib.gemm_mkl_rms_norm_ex.argtypes = [vp, vp, vp, i64, i64, ctypes.c_float, i32, vp, i32]
+    lib.gemm_mkl_rms_norm_ex.restype = i32
+    lib.gemm_mkl_rms_norm_variant.argtypes = [i64, i64, i32, i32]
+    lib.gemm_mkl_rms_norm_variant.restype = i32
+    lib.gemm_mkl_rms_norm_num_variants.argtypes = []
+    lib.gemm_mkl_rms_norm_num_variants.restype = i32
+    lib.gemm_mkl_rms_norm_variant_name.argtypes = [i32]
+    lib.gemm_mkl_rms_norm_variant_name.restype = ctypes.c_char_p
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -178,6 +193,25 @@ def grouped_config(G, total_m, N, K, dtype, epilogue, opts: Opts | None = None) 
     if st < 0:
         raise GemmMklError(st, status_string(st))
     return st
+
+
+def gemm_mkl_rms_norm(x_ptr, w_ptr, y_ptr, rows, hidden, eps, dtype, stream=None, variant=-1) -> int:
+    """The RMSNorm entry point (gemm_mkl_rms_norm_ex): device pointers as ints
+    (w_ptr None for no weight), returns the status."""
+    return load().gemm_mkl_rms_norm_ex(x_ptr, w_ptr, y_ptr, rows, hidden, eps, dtype, stream, variant)
+
+
+def rms_norm_variant(rows, hidden, dtype, aligned=True) -> int:
+    """Variant gemm_mkl_rms_norm picks for these sizes (raises on a negative status)."""
+    st = load().gemm_mkl_rms_norm_variant(rows, hidden, dtype, 1 if aligned else 0)
+    if st < 0:
+        raise GemmMklError(st, status_string(st))
+    return st
+
+
+def rms_norm_variant_names() -> list[str]:
+    lib = load()
+    return [lib.gemm_mkl_rms_norm_variant_name(i).decode() for i in range(lib.gemm_mkl_rms_norm_num_variants())]
 
 
 def get_plan(M, N, K, L, dtype, epilogue, opts: Opts | None = None) -> dict:
@@ -306,6 +340,40 @@ def gemm_grouped(a, b, offs, epilogue: str = "identity", out=None, *, prefetch_s
     with torch.cuda.device(a.device):
         st = gemm_mkl_grouped(a.data_ptr(), b.data_ptr(), out.data_ptr(), offs.data_ptr(), G, total_m, N, K,
                               _torch_dtype_code(a), EPILOGUE_CODES[epilogue], s.cuda_stream, opts)
+    if st != 0:
+        raise GemmMklError(st, status_string(st))
+    return out
+
+
+def rms_norm(x, weight=None, eps: float = 1e-6, out=None, *, variant: int = -1, stream=None):
+    """RMSNorm over the last axis on the GPU through libgemm_mkl:
+    y = x * rsqrt(mean(x^2) + eps) * weight, computed in fp32, rounded once to
+    x's dtype.
+
+    x: [..., hidden] contiguous; weight: [hidden] of x's dtype or None (no
+    weight); out: like x, may be x itself (in place).
+    """
+    import torch
+
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
+        raise ValueError("x must be a torch tensor on a GPU")
+    if x.dim() < 1 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous tensor with at least one dimension")
+    hidden = x.shape[-1]
+    rows = x.numel() // hidden if hidden else 0
+    if weight is not None:
+        if not isinstance(weight, torch.Tensor) or weight.device != x.device or weight.dtype != x.dtype \
+                or tuple(weight.shape) != (hidden,) or not weight.is_contiguous():
+            raise ValueError("weight must be a contiguous [hidden] tensor of x's dtype on x's GPU")
+    if out is None:
+        out = torch.empty_like(x)
+    elif tuple(out.shape) != tuple(x.shape) or out.dtype != x.dtype or not out.is_contiguous() \
+            or out.device != x.device:
+        raise ValueError("out must be a contiguous tensor shaped and typed like x on x's GPU")
+    s = stream if stream is not None else torch.cuda.current_stream(x.device)
+    with torch.cuda.device(x.device):
+        st = gemm_mkl_rms_norm(x.data_ptr(), weight.data_ptr() if weight is not None else None, out.data_ptr(),
+                               rows, hidden, float(eps), _torch_dtype_code(x), s.cuda_stream, variant)
     if st != 0:
         raise GemmMklError(st, status_string(st))
     return out

@@ -20,7 +20,7 @@ LIB = os.path.join(LIBDIR, "libgemm_mkl.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
 ARCH = "gfx950"
-UNITS = ["gemm_api.hip", "inst_f32.hip", "inst_f16.hip", "inst_bf16.hip"]
+UNITS = ["gemm_api.hip", "inst_f32.hip", "inst_f16.hip", "inst_bf16.hip", "rms_norm.hip"]
 HEADERS = ["gemm_kernels.hpp", "configs.hpp"]
 
 

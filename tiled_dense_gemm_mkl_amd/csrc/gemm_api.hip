@@ -648,6 +648,11 @@ int run_grouped(const void *A, const void *B, void *C, const int32_t *offs, int6
 
 }  // namespace
 
+namespace gmk {
+// Records a HIP error of another unit's launch for gemm_mkl_status_string.
+void note_hip_error(hipError_t e) { t_last_hip = e; }
+}  // namespace gmk
+
 extern "C" {
 
 void gemm_mkl_opts_init(gemm_mkl_opts *o)

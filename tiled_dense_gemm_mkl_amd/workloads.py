@@ -1,6 +1,6 @@
-"""Seeded synthetic inputs for the GEMM workloads.
+"""Seeded synthetic inputs for the GEMM and RMSNorm workloads.
 
-This module holds no GEMM arithmetic.  It only draws random operands and
+This module holds no GEMM or RMSNorm arithmetic.  It only draws random operands and
 stores them in the operand dtype, so that the GPU path and the CPU oracle can
 be fed the very same stored bits.
 
@@ -176,6 +176,59 @@ def make_grouped_inputs(w: GroupedWorkload | str, integer: bool = False):
     _, B = random_operands(w.dtype, 1, w.N, w.K, w.G, seed + 1, w.dist_a, w.dist_b, integer)
     offs = np.cumsum(group_sizes(w.G, w.total_m, w.seed)).astype(np.int32)
     return A[0], B, offs
+
+
+@dataclass(frozen=True)
+class RmsNormWorkload:
+    key: str
+    name: str
+    dtype: str        # x, weight and y
+    rows: int
+    hidden: int
+    eps: float
+    weight: tuple     # ("ones",) | ("normal", mean, std)
+    seed: int
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """x read once, y written once, the weight read once."""
+        es = 4 if self.dtype == "f32" else 2
+        return es * (2 * self.rows * self.hidden + self.hidden)
+
+
+RMSNORM_WORKLOADS = {
+    w.key: w
+    for w in [
+        RmsNormWorkload(
+            "rmsnorm_f32_32x2048",
+            "fp32 RMSNorm(2048) over 32 rows of N(0,1), unit weight, eps 1e-6 (the compiler page's example)",
+            "f32", 32, 2048, 1e-6, ("ones",), 7),
+        RmsNormWorkload(
+            "rmsnorm_f32_65536x2048",
+            "fp32 RMSNorm(2048) over 65536 rows of N(0,1), weight 1 + N(0,0.1^2), eps 1e-6",
+            "f32", 65536, 2048, 1e-6, ("normal", 1.0, 0.1), 8),
+        RmsNormWorkload(
+            "rmsnorm_bf16_65536x3584",
+            "bf16 RMSNorm(3584) over 65536 rows of N(0,1), weight 1 + N(0,0.1^2), eps 1e-6",
+            "bf16", 65536, 3584, 1e-6, ("normal", 1.0, 0.1), 9),
+    ]
+}
+
+
+def make_rms_inputs(w: RmsNormWorkload | str, rows: int | None = None):
+    """x [rows, hidden] ~ N(0, 1) and the weight [hidden], as stored bits.
+    The weight is drawn first, then the rows in order, so a prefix of the rows
+    (rows < w.rows) is the same prefix of the full input."""
+    if isinstance(w, str):
+        w = RMSNORM_WORKLOADS[w]
+    rows = w.rows if rows is None else rows
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    if w.weight[0] == "ones":
+        wt = np.ones(w.hidden)
+    else:
+        wt = w.weight[1] + w.weight[2] * rng.standard_normal(w.hidden)
+    x = rng.standard_normal((rows, w.hidden))
+    return to_storage(x, w.dtype), to_storage(wt, w.dtype)
 
 
 def storage_to_torch(x: np.ndarray, dtype: str):
