@@ -68,28 +68,78 @@ def measured_traffic(workload_key: str, kernel: str, sources=None):
 
 
 def cpu_baseline(w, A, B, budget_s: float = 10.0):
-    """The oracle as it stands, on this host's cores: whole calls on the full
-    workload, repeated until about budget_s seconds of CPU work (at least 3);
-    the median call time gives the rate."""
+    """The oracle as it stands, on this host's cores, on a bounded sample of
+    the workload: the first m rows of A in every batch (all of them when a
+    whole call takes under about 2 s), repeated until about budget_s seconds
+    of CPU work (at least 3 calls); the median call time gives the rate."""
+    import numpy as np
+
     import oracle
 
     oracle.load()
+    # one probe call on a few rows sizes the sample
+    m = min(w.M, 8)
+    t0 = time.perf_counter()
+    oracle.gemm64(np.ascontiguousarray(A[:, :m]), B, w.dtype, w.epilogue)
+    per_row = (time.perf_counter() - t0) / m
+    m = int(max(1, min(w.M, 2.0 / max(per_row, 1e-9))))
+    As = np.ascontiguousarray(A[:, :m])
+    flops = 2 * m * w.N * w.K * w.L
     times = []
     while len(times) < 3 or (sum(times) < budget_s and len(times) < 200):
         t0 = time.perf_counter()
-        y = oracle.gemm64(A, B, w.dtype, w.epilogue)
+        y = oracle.gemm64(As, B, w.dtype, w.epilogue)
         times.append(time.perf_counter() - t0)
         del y
     threads = oracle.threads()
     t = sorted(times)[len(times) // 2]
+    what = "the full workload" if m == w.M else f"the first {m} of {w.M} rows of A in every batch"
     return {
-        "value": round(w.flops / t / 1e12, 6),
+        "value": round(flops / t / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{len(times)} whole calls on the full workload ({w.M}x{w.N}x{w.K}, L={w.L}), "
+        "sample": f"{len(times)} calls on {what} ({m}x{w.N}x{w.K}, L={w.L}), "
                   f"binary64 dot products, median {t:.3f} s per call",
     }
+
+
+def device_info(dev) -> dict:
+    """Name, compute units and clock of the GPU as the runtime reports them."""
+    import torch
+
+    pr = torch.cuda.get_device_properties(dev)
+    info = {"name": pr.name, "compute_units": pr.multi_processor_count,
+            "arch": getattr(pr, "gcnArchName", None)}
+    clk = getattr(pr, "clock_rate", None)   # kHz, where the runtime reports it
+    if clk:
+        info["clock_mhz"] = round(clk / 1e3)
+    return info
+
+
+def cold_cache_rate(w, a, b, c, step_ptrs, steps: int) -> dict:
+    """Throughput when every call reads A and B from HBM: calls rotate over
+    enough copies of A and B that their total exceeds 512 MiB, twice the
+    256 MiB memory-side cache, so no call finds its operands cached."""
+    import math
+
+    import torch
+
+    nbytes = a.numel() * a.element_size() + b.numel() * b.element_size()
+    copies = max(2, math.ceil((512 << 20) / nbytes) + 1)
+    bufs = [(a.clone(), b.clone()) for _ in range(copies)]
+    ptrs = [(x.data_ptr(), y.data_ptr()) for x, y in bufs]
+    for i in range(copies):
+        step_ptrs(*ptrs[i])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step_ptrs(*ptrs[i % copies])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    del bufs
+    return {"value": round(w.flops / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "ms_per_step": round(ms, 6),
+            "copies": copies, "bytes_rotated": copies * nbytes}
 
 
 def copy_calibration(mib: int, steps: int) -> int:
@@ -275,6 +325,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time calls that rotate over copies of A and B larger than the caches")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run only a device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -311,10 +363,13 @@ def main() -> int:
     sptr = stream.cuda_stream
     ap_, bp_, cp_ = a.data_ptr(), b.data_ptr(), c.data_ptr()
 
-    def step():
-        st = gm.gemm_mkl(ap_, bp_, cp_, w.M, w.N, w.K, w.L, dcode, ecode, sptr)
+    def step_ptrs(ap, bp):
+        st = gm.gemm_mkl(ap, bp, cp_, w.M, w.N, w.K, w.L, dcode, ecode, sptr)
         if st != 0:
             raise gm.GemmMklError(st, gm.status_string(st))
+
+    def step():
+        step_ptrs(ap_, bp_)
 
     for _ in range(args.warmup):
         step()
@@ -379,6 +434,9 @@ def main() -> int:
             "launch_us": round(ev_ms_per_launch * 1e3, 3),
         },
     }
+    result["device"] = device_info(dev)
+    if args.cold:
+        result["cold_cache"] = cold_cache_rate(w, a, b, c, step_ptrs, args.steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, A, B)
     print(json.dumps(result), flush=True)

@@ -634,6 +634,7 @@ int run_grouped(const void *A, const void *B, void *C, const int32_t *offs, int6
     gp.tiles_n = (int32_t)tiles_n;
     gp.row_tiles = (int32_t)row_tiles;
     gp.total_chunks = (int32_t)((K * es + c.rb - 1) / c.rb);
+    gp.group_m = std::max<int32_t>(1, (int32_t)env().group_m);
     if (env().log)
         std::fprintf(stderr, "gemm_mkl_grouped: G=%lld rows=%lld N=%lld K=%lld dtype=%d epi=%d -> %s P=%d grid=%lld\n",
                      (long long)G, (long long)total_m, (long long)N, (long long)K, dtype, epilogue, c.name,

@@ -778,7 +778,13 @@ struct TileCore {
             if (gm >= M) continue;
             OT *dst = out + gm * N + gn;
             if (vec16 && gn + EPC <= N) {
-                *reinterpret_cast<i32x4 *>(dst) = v;
+                // the result is not read again by this kernel: a non-temporal
+                // store (measured 16.5 -> 16.0 us on the 512x5632x2048 bf16
+                // shape); split-K partials stay cached for the reduction
+                if constexpr (MODE == MODE_PARTIAL)
+                    *reinterpret_cast<i32x4 *>(dst) = v;
+                else
+                    __builtin_nontemporal_store(v, reinterpret_cast<i32x4 *>(dst));
             } else {
                 OT e[EPC];
                 __builtin_memcpy(e, &v, 16);
@@ -956,6 +962,7 @@ struct GroupedParams {
     int32_t tiles_n;
     int32_t row_tiles;     // row tiles the grid covers (an upper bound on the groups' sum)
     int32_t total_chunks;
+    int32_t group_m;       // raster group height inside a group
 };
 
 // Row tile `tr` of the concatenation of every group's row tiles -> (group,
@@ -1013,12 +1020,20 @@ __global__ __launch_bounds__((WAVES_M *WAVES_N + NP) * 64) void gemm_grouped_ker
 {
     typedef TileCore<T, BM, BN, RB, WAVES_M, WAVES_N, MF, P, 1, NP> Core;
     __shared__ __attribute__((aligned(1024))) char smem[Core::LDS_BYTES];
+    // Group-major order: group g owns the R_g * tiles_n consecutive ids after
+    // those of groups 0 .. g-1 (R_g = its row tiles), and inside a group the
+    // tiles follow the usual raster.  Tiles that share a column block of B[g]
+    // then run close together, on one XCD, and no raster group mixes two
+    // groups' B.
     const int t = xcd_remap(blockIdx.x, gridDim.x);
-    int tr, tn;
-    raster(t, gp.row_tiles, gp.tiles_n, 4, tr, tn);
-    int g, tm, row0, rows;
-    find_group<BM>(gp, tr, g, tm, row0, rows);
+    const int v = t / gp.tiles_n;   // the v-th row tile of the concatenated groups
+    int g, tv, row0, rows;
+    find_group<BM>(gp, v, g, tv, row0, rows);
     if (g < 0) return;   // past the groups' row tiles (the same for every wave)
+    const int rg = (rows + BM - 1) / BM;
+    const int u = t - (v - tv) * gp.tiles_n;   // id inside the group
+    int tm, tn;
+    raster(u, rg, gp.tiles_n, gp.group_m, tm, tn);
     Core c;
     c.init(smem);
     TileParams p;
