@@ -112,6 +112,15 @@ int gemm_mkl(const void *A, const void *B, void *C,
  *   (tile, K-chunk) units; tiles cut between workgroups are summed in a fixed
  *   order, so results stay bitwise reproducible).  The automatic plan uses
  *   stream-K only when GEMM_MKL_STREAMK=-1 is set in the environment.
+ *   GEMM_MKL_OPT_PERSISTENT / GEMM_MKL_OPT_NO_PERSISTENT force / forbid the
+ *   persistent grid (one workgroup per compute unit, each taking every
+ *   G-th tile and running one prefetch ring across its tiles, so a tile's
+ *   first loads overlap the end of the tile before it).  It exists for the
+ *   producer-wave configurations, without a K split; each tile is computed
+ *   exactly as by the data-parallel grid (same chunk order), so results are
+ *   bitwise equal to it.  The automatic plan does not use it (it measured no
+ *   faster than the data-parallel grid); GEMM_MKL_PERSISTENT=-1 lets the plan
+ *   take it whenever there are more tiles than compute units, =1 always.
  * workspace / workspace_bytes: caller-owned device memory for split-K or
  *   stream-K partial sums (NULL = use the library's internal workspace).  It
  *   must hold the plan's workspace_bytes (gemm_mkl_get_plan) and be 256-byte
@@ -123,7 +132,9 @@ int gemm_mkl(const void *A, const void *B, void *C,
  * The environment variables GEMM_MKL_FORCE_CONFIG, GEMM_MKL_STAGES and
  * GEMM_MKL_SPLIT_K supply the same three choices when opts leaves them
  * automatic (for sweeps); GEMM_MKL_STREAMK=0/1/-1 never / always / by model
- * uses stream-K; GEMM_MKL_GROUP_M sets the tile-raster group height;
+ * uses stream-K; GEMM_MKL_PERSISTENT=0/1/-1 never (default) / always / when
+ * there are more tiles than compute units uses the persistent grid; GEMM_MKL_GROUP_M
+ * sets the tile-raster group height;
  * GEMM_MKL_LOG=1 prints each call's plan to stderr;
  * GEMM_MKL_WORKSPACE_LIMIT=<bytes> caps the internal workspace.  They are
  * read once, at the first call.  Plans are cached per (sizes, dtype, pointer
@@ -144,7 +155,11 @@ enum {
     GEMM_MKL_OPT_STREAMK = 2,       /* use the stream-K kernel (NOT_AVAILABLE if no
                                        configuration of the dtype has one, or with
                                        split_k > 1) */
-    GEMM_MKL_OPT_NO_STREAMK = 4     /* never use the stream-K kernel */
+    GEMM_MKL_OPT_NO_STREAMK = 4,    /* never use the stream-K kernel */
+    GEMM_MKL_OPT_PERSISTENT = 8,    /* use the persistent grid (NOT_AVAILABLE unless the
+                                       chosen configuration has one, with split_k 1 and
+                                       its own prefetch depth) */
+    GEMM_MKL_OPT_NO_PERSISTENT = 16 /* never use the persistent grid */
 };
 
 /* Initialise opts to "all automatic". */
@@ -258,6 +273,8 @@ typedef struct gemm_mkl_plan {
     size_t workspace_bytes;   /* 0 when split_k == 1 and not stream-K */
     int32_t streamk;          /* 1 if the stream-K kernel is used (grid = workgroups) */
     int32_t counter_bytes;    /* stream-K: leading workspace bytes holding counters */
+    int32_t persistent;       /* 1 if the persistent grid is used (grid = workgroups) */
+    int32_t reserved;
 } gemm_mkl_plan;
 
 int gemm_mkl_get_plan(int64_t M, int64_t N, int64_t K, int64_t L,

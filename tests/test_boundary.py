@@ -204,9 +204,9 @@ def test_streamk_plans(lib):
 
 def test_ctypes_struct_sizes_match_header(lib):
     # gemm_mkl_opts: 4 x int32, pointer, size_t
-    # gemm_mkl_plan: 4 x int32, int64, 4 x int32, size_t, 2 x int32
+    # gemm_mkl_plan: 4 x int32, int64, 4 x int32, size_t, 4 x int32
     assert ctypes.sizeof(gm._binding.Opts) == 32
-    assert ctypes.sizeof(gm._binding.Plan) == 56
+    assert ctypes.sizeof(gm._binding.Plan) == 64
 
 
 def test_streamk_only_where_instantiated(lib):
@@ -341,3 +341,42 @@ def test_rms_norm_variant_choice(lib):
     assert pick(4, 2048, F32, False) == "general"       # unaligned pointers
     with pytest.raises(gm.GemmMklError):
         gm.rms_norm_variant(4, 64, 9)
+
+
+# ------------------------------------------------------------------ persistent grid
+
+def test_persistent_plans(lib):
+    names = gm.config_names()
+    cid = names.index("bf16 128x128 k64 waves2x2+4p mfma32")
+    # opt-in: the automatic plan keeps the data-parallel grid
+    p = gm.get_plan(4096, 5632, 2048, 1, BF16, RELU, gm.make_opts(config_id=cid))
+    assert p["persistent"] == 0 and p["grid"] == 1408
+    # forced with more tiles than compute units: one workgroup per CU
+    p = gm.get_plan(4096, 5632, 2048, 1, BF16, RELU, gm.make_opts(config_id=cid, persistent=True))
+    assert p["persistent"] == 1 and p["grid"] == 256 and p["split_k"] == 1 and p["prefetch_stages"] == 3
+    # forced on a small problem: one workgroup per tile
+    p = gm.get_plan(300, 200, 2112, 2, BF16, SILU, gm.make_opts(config_id=cid, persistent=True))
+    assert p["persistent"] == 1 and p["grid"] == 3 * 2 * 2
+    # forbidden, or with another depth or a split: not persistent
+    assert gm.get_plan(4096, 5632, 2048, 1, BF16, RELU, gm.make_opts(config_id=cid, persistent=False))["persistent"] == 0
+    assert gm.get_plan(4096, 5632, 2048, 1, BF16, RELU, gm.make_opts(config_id=cid, prefetch_stages=4))["persistent"] == 0
+    assert gm.get_plan(4096, 5632, 2048, 1, BF16, RELU, gm.make_opts(config_id=cid, split_k=2))["persistent"] == 0
+
+
+def test_persistent_forced_where_unavailable(lib):
+    names = gm.config_names()
+    f32 = [i for i, n in enumerate(names) if n.startswith("f32")][0]
+    for o in (gm.make_opts(config_id=f32, persistent=True),
+              gm.make_opts(config_id=names.index("bf16 128x128 k64 waves2x2+4p mfma32"), persistent=True,
+                           prefetch_stages=4),
+              gm.make_opts(config_id=names.index("bf16 128x128 k64 waves2x2+4p mfma32"), persistent=True,
+                           split_k=2)):
+        dt = F32 if o.config_id == f32 else BF16
+        with pytest.raises(gm.GemmMklError) as e:
+            gm.get_plan(1024, 1024, 512, 1, dt, ID, o)
+        assert e.value.status == -6
+    o = gm.make_opts(persistent=True)
+    o.flags |= 16   # with GEMM_MKL_OPT_NO_PERSISTENT
+    with pytest.raises(gm.GemmMklError) as e:
+        gm.get_plan(1024, 1024, 512, 1, BF16, ID, o)
+    assert e.value.status == -1

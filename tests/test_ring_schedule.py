@@ -22,8 +22,12 @@ ring slot off by one, a missing drain) must each be caught.
 import pytest
 
 
-def schedule(KSW, NMF, NRD, LOADS, P, nk, producers=False, mut=None):
-    """Per-role event lists of the ring over nk chunks (the kernel's order)."""
+def schedule(KSW, NMF, NRD, LOADS, P, nk, producers=False, mut=None, tile_chunks=0):
+    """Per-role event lists of the ring over nk chunks (the kernel's order).
+    tile_chunks > 0 models the persistent ring: the nk units are tiles of
+    tile_chunks chunks each, and after the barrier that ends a tile's last
+    unit the MFMA waves stage the tile, every wave meets at one more barrier,
+    and the MFMA waves read the staged tile back (run_persistent)."""
     RA = 1 if (NMF >= 8 or KSW < 4) else KSW - 1
     NB = RA + 1
     SLOTS = P + 1
@@ -96,6 +100,8 @@ def schedule(KSW, NMF, NRD, LOADS, P, nk, producers=False, mut=None):
         prod.append(("wait", WAIT))
         if mut != "no_barrier":
             prod.append(("bar", False))
+        if tile_chunks and i % tile_chunks == tile_chunks - 1 and mut != "no_stage_barrier":
+            prod.append(("bar", False))
         fill = (fill + 1) % SLOTS
     prod.append(("wait", 0))
     mma.append(("bar", False))
@@ -118,6 +124,12 @@ def schedule(KSW, NMF, NRD, LOADS, P, nk, producers=False, mut=None):
                 mma.append(("read", rs, rc, tks, t % NB))
         if mut != "no_barrier":
             mma.append(("bar", False))
+        if tile_chunks and i % tile_chunks == tile_chunks - 1:
+            k = i // tile_chunks
+            mma.append(("stage_w", k))
+            if mut != "no_stage_barrier":
+                mma.append(("bar", False))
+            mma.append(("stage_r", k))
         slot = nxt
     return [prod, mma], KSW * NMF, KSW * NRD
 
@@ -169,6 +181,23 @@ def check(roles, mfma_per_chunk, reads_per_chunk, LOADS, nk):
     for k in loaders:
         for b in range(len(visible)):
             content[b].update(states[k][b][2])
+    # the staging area of the persistent ring: a tile is read back only after
+    # a barrier that every MFMA wave reached after writing it, and the next
+    # tile is written only after a barrier that every MFMA wave reached after
+    # reading the previous one (all MFMA waves run the same program, so the
+    # barrier counts of one program decide)
+    for ev in roles:
+        b, at = 0, {}
+        for e in ev:
+            if e[0] == "bar":
+                b += 1
+            elif e[0] in ("stage_w", "stage_r"):
+                at[(e[0], e[1])] = b
+        for (kind, k), bw in at.items():
+            if kind == "stage_w":
+                assert at[("stage_r", k)] > bw, f"staged tile {k} read before every wave wrote it"
+                if ("stage_r", k - 1) in at:
+                    assert bw > at[("stage_r", k - 1)], f"tile {k} staged over tile {k - 1} still being read"
     # replay each role against the barrier states
     for ev in roles:
         b = -1
@@ -221,6 +250,31 @@ def test_ring_schedule_has_no_hazard(shape, P, producers):
     for nk in (1, 2, 3, 4, 5, 7, 16):
         roles, mpc, rpc = schedule(KSW, NMF, NRD, LOADS, P, nk, producers)
         check(roles, mpc, rpc, LOADS, nk)
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("P", [2, 3, 4])
+@pytest.mark.parametrize("tile_chunks", [1, 2, 3, 5])
+def test_persistent_ring_has_no_hazard(shape, P, tile_chunks):
+    KSW, NMF, NRD, LOADS = shape
+    if LOADS * P >= 64:
+        pytest.skip("beyond the vmcnt range")
+    for ntiles in (1, 2, 3, 7):
+        nk = ntiles * tile_chunks
+        roles, mpc, rpc = schedule(KSW, NMF, NRD, LOADS, P, nk, True, tile_chunks=tile_chunks)
+        check(roles, mpc, rpc, LOADS, nk)
+
+
+def test_persistent_missing_stage_barrier_is_caught():
+    caught = False
+    for tile_chunks in (1, 2):
+        roles, mpc, rpc = schedule(4, 4, 4, 8, 3, 4 * tile_chunks, True, mut="no_stage_barrier",
+                                   tile_chunks=tile_chunks)
+        try:
+            check(roles, mpc, rpc, 8, 4 * tile_chunks)
+        except AssertionError:
+            caught = True
+    assert caught
 
 
 @pytest.mark.parametrize("mut,producers,P", [

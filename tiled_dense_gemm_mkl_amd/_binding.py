@@ -25,6 +25,8 @@ STATUS = {
 OPT_FORCE_GENERAL = 1
 OPT_STREAMK = 2
 OPT_NO_STREAMK = 4
+OPT_PERSISTENT = 8
+OPT_NO_PERSISTENT = 16
 
 DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16}
 EPILOGUE_CODES = {"identity": EPI_IDENTITY, "relu": EPI_RELU, "silu": EPI_SILU}
@@ -63,6 +65,8 @@ class Plan(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("streamk", ctypes.c_int32),
         ("counter_bytes", ctypes.c_int32),
+        ("persistent", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
     def as_dict(self) -> dict:
@@ -147,7 +151,7 @@ def status_string(status: int) -> str:
 
 
 def make_opts(prefetch_stages=None, split_k=None, config_id=None, force_general=False,
-              workspace_ptr=None, workspace_bytes=0, streamk=None) -> Opts:
+              workspace_ptr=None, workspace_bytes=0, streamk=None, persistent=None) -> Opts:
     o = Opts()
     load().gemm_mkl_opts_init(ctypes.byref(o))
     if prefetch_stages is not None:
@@ -162,6 +166,10 @@ def make_opts(prefetch_stages=None, split_k=None, config_id=None, force_general=
         o.flags |= OPT_STREAMK
     elif streamk is False:
         o.flags |= OPT_NO_STREAMK
+    if persistent is True:
+        o.flags |= OPT_PERSISTENT
+    elif persistent is False:
+        o.flags |= OPT_NO_PERSISTENT
     if workspace_ptr is not None:
         o.workspace = int(workspace_ptr)
         o.workspace_bytes = int(workspace_bytes)
@@ -250,7 +258,7 @@ def _torch_dtype_code(t) -> int:
 
 
 def gemm(a, b, epilogue: str = "identity", out=None, *, prefetch_stages=None, split_k=None,
-         config_id=None, force_general=False, workspace=None, stream=None, streamk=None):
+         config_id=None, force_general=False, workspace=None, stream=None, streamk=None, persistent=None):
     """C = epilogue(a @ b^T) per batch, on the GPU through libgemm_mkl.
 
     a: [L, M, K] or [M, K]; b: [L, N, K] or [N, K] (same dtype, on one GPU,
@@ -291,7 +299,7 @@ def gemm(a, b, epilogue: str = "identity", out=None, *, prefetch_stages=None, sp
     ws_ptr = ws_bytes = None
     if workspace is not None:
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    opts = make_opts(prefetch_stages, split_k, config_id, force_general, ws_ptr, ws_bytes or 0, streamk)
+    opts = make_opts(prefetch_stages, split_k, config_id, force_general, ws_ptr, ws_bytes or 0, streamk, persistent)
     s = stream if stream is not None else torch.cuda.current_stream(a.device)
     with torch.cuda.device(a.device):
         st = gemm_mkl_ex(a3.data_ptr(), b3.data_ptr(), out3.data_ptr(), M, N, K, L,

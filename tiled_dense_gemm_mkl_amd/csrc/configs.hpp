@@ -36,6 +36,8 @@ struct ConfigEntry {
     StreamKLaunchFn sk[kMaxPrefetch + 1][3];    // stream-K by epilogue, null where not instantiated
     GroupedLaunchFn grouped[3];                 // grouped GEMM by epilogue (depth grouped_p), or null
     int grouped_p;
+    TileLaunchFn persist[3];                    // persistent grid by epilogue (depth persist_p), or null
+    int persist_p;
 };
 
 struct DtypeKernels {
@@ -84,6 +86,27 @@ ConfigEntry with_grouped(ConfigEntry e)
     e.grouped[MODE_RELU] = &launch_grouped<T, BM, BN, RB, WMW, WNW, MF, P, MODE_RELU, NP>;
     e.grouped[MODE_SILU] = &launch_grouped<T, BM, BN, RB, WMW, WNW, MF, P, MODE_SILU, NP>;
     e.grouped_p = P;
+    return e;
+}
+
+template <class T, int BM, int BN, int RB, int WMW, int WNW, int MF, int P, int MODE, int NP>
+hipError_t launch_persistent(const TileParams &p, int grid, hipStream_t stream)
+{
+    hipLaunchKernelGGL((gemm_persistent_kernel<T, BM, BN, RB, WMW, WNW, MF, P, MODE, NP>), dim3(grid),
+                       dim3((WMW * WNW + NP) * 64), 0, stream, p);
+    return hipGetLastError();
+}
+
+// Adds the persistent-grid kernels (prefetch depth P, NP producer waves) to an
+// entry made by make_entry_kp with the same tile and wave grid.
+template <class T, int BM, int BN, int RB, int WMW, int WNW, int NP, int MF, int P>
+ConfigEntry with_persistent(ConfigEntry e)
+{
+    static_assert(NP > 0 && P >= 2, "the persistent ring uses producer waves");
+    e.persist[MODE_IDENTITY] = &launch_persistent<T, BM, BN, RB, WMW, WNW, MF, P, MODE_IDENTITY, NP>;
+    e.persist[MODE_RELU] = &launch_persistent<T, BM, BN, RB, WMW, WNW, MF, P, MODE_RELU, NP>;
+    e.persist[MODE_SILU] = &launch_persistent<T, BM, BN, RB, WMW, WNW, MF, P, MODE_SILU, NP>;
+    e.persist_p = P;
     return e;
 }
 

@@ -61,13 +61,14 @@ int env_int(const char *name, int dflt)
 
 // The environment overrides, read once, at the first call that needs them.
 struct EnvSettings {
-    int force_config, stages, split_k, streamk, group_m, log;
+    int force_config, stages, split_k, streamk, group_m, log, persistent;
     bool has_ws_limit;
     size_t ws_limit;
     EnvSettings()
         : force_config(env_int("GEMM_MKL_FORCE_CONFIG", -1)), stages(env_int("GEMM_MKL_STAGES", -1)),
           split_k(env_int("GEMM_MKL_SPLIT_K", 0)), streamk(env_int("GEMM_MKL_STREAMK", 0)),
-          group_m(env_int("GEMM_MKL_GROUP_M", 4)), log(env_int("GEMM_MKL_LOG", 0)), has_ws_limit(false), ws_limit(0)
+          group_m(env_int("GEMM_MKL_GROUP_M", 4)), log(env_int("GEMM_MKL_LOG", 0)),
+          persistent(env_int("GEMM_MKL_PERSISTENT", 0)), has_ws_limit(false), ws_limit(0)
     {
         const char *lim = std::getenv("GEMM_MKL_WORKSPACE_LIMIT");
         if (lim && *lim) {
@@ -97,6 +98,7 @@ struct Plan {
     int S = 1;
     bool general = false;
     bool streamk = false;
+    bool persistent = false;       // persistent grid with one ring across each workgroup's tiles
     int64_t sk_units = 0;          // stream-K: tiles (all batches) * chunks per tile
     size_t sk_counter_bytes = 0;   // stream-K: per-tile counters, 256-byte padded
     int64_t grid = 0;
@@ -123,9 +125,12 @@ int check_args(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, int epilog
         if (o->prefetch_stages < -1) return GEMM_MKL_STATUS_INVALID_VALUE;
         if (o->split_k < 0) return GEMM_MKL_STATUS_INVALID_VALUE;
         if (o->config_id < -1) return GEMM_MKL_STATUS_INVALID_VALUE;
-        const int32_t known = GEMM_MKL_OPT_FORCE_GENERAL | GEMM_MKL_OPT_STREAMK | GEMM_MKL_OPT_NO_STREAMK;
+        const int32_t known = GEMM_MKL_OPT_FORCE_GENERAL | GEMM_MKL_OPT_STREAMK | GEMM_MKL_OPT_NO_STREAMK |
+                              GEMM_MKL_OPT_PERSISTENT | GEMM_MKL_OPT_NO_PERSISTENT;
         if (o->flags & ~known) return GEMM_MKL_STATUS_INVALID_VALUE;
         if ((o->flags & GEMM_MKL_OPT_STREAMK) && (o->flags & GEMM_MKL_OPT_NO_STREAMK))
+            return GEMM_MKL_STATUS_INVALID_VALUE;
+        if ((o->flags & GEMM_MKL_OPT_PERSISTENT) && (o->flags & GEMM_MKL_OPT_NO_PERSISTENT))
             return GEMM_MKL_STATUS_INVALID_VALUE;
         if (o->workspace == nullptr && o->workspace_bytes != 0) return GEMM_MKL_STATUS_INVALID_VALUE;
         if (o->workspace && (reinterpret_cast<uintptr_t>(o->workspace) & 255)) return GEMM_MKL_STATUS_INVALID_VALUE;
@@ -223,6 +228,16 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
     // stream-K then only runs when forced, and never together with a split
     if (forced_s > 1 && sk_mode == 1) return GEMM_MKL_STATUS_NOT_AVAILABLE;
     if (forced_s >= 1 && sk_mode != 1) sk_mode = 0;
+    // persistent grid: -1 whenever there are more tiles than compute units, 0 never
+    // (the default: it measured no faster than the data-parallel grid), 1 always
+    int pers_mode = env().persistent;
+    if (o && (o->flags & GEMM_MKL_OPT_PERSISTENT)) pers_mode = 1;
+    if (o && (o->flags & GEMM_MKL_OPT_NO_PERSISTENT)) pers_mode = 0;
+    if (pers_mode == 1) {   // a forced persistent grid never splits K
+        if (forced_s > 1 || sk_mode == 1) return GEMM_MKL_STATUS_NOT_AVAILABLE;
+        forced_s = 1;
+        sk_mode = 0;
+    }
 
     if (forced_cfg >= (int)R.table.size()) return GEMM_MKL_STATUS_NOT_AVAILABLE;
     if (forced_cfg >= 0 && R.table[forced_cfg].dtype != dtype) return GEMM_MKL_STATUS_NOT_AVAILABLE;
@@ -330,6 +345,21 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
         plan->sk_counter_bytes = ((size_t)tiles_all * 4 + 255) / 256 * 256;
         // [counters][2 partial tiles per workgroup]
         plan->ws_bytes = plan->sk_counter_bytes + (size_t)2 * plan->grid * c.bm * c.bn * 4;
+    }
+    // The persistent grid: one workgroup per compute unit, each running one
+    // ring across its tiles, so that a tile's first loads overlap the end of
+    // the tile before it.  It can only pay off with more tiles than compute
+    // units (a single round has no next tile to overlap); measured on MI355X
+    // it was no faster than the data-parallel grid at depth 4 (the staging
+    // area leaves room for depth 3 only), so it runs only when asked for.
+    const int64_t tiles_all = (int64_t)plan->tiles_m * plan->tiles_n * L;
+    const bool pers_ok = c.persist[0] != nullptr && plan->S == 1 && !best_sk && total_chunks > 0 &&
+                         (forced_p < 0 || forced_p == c.persist_p) && tiles_all <= INT32_MAX;
+    if (pers_mode == 1 && !pers_ok) return GEMM_MKL_STATUS_NOT_AVAILABLE;
+    if (pers_ok && (pers_mode == 1 || (pers_mode == -1 && tiles_all > kNumCUs))) {
+        plan->persistent = true;
+        plan->P = c.persist_p;
+        plan->grid = std::min<int64_t>(tiles_all, kNumCUs);
     }
     return GEMM_MKL_STATUS_OK;
 }
@@ -494,7 +524,7 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
         std::fprintf(stderr, "gemm_mkl: M=%lld N=%lld K=%lld L=%lld dtype=%d epi=%d -> %s P=%d S=%d%s grid=%lld\n",
                      (long long)M, (long long)N, (long long)K, (long long)L, dtype, epilogue,
                      plan.general ? "general" : R.table[plan.config_id].name, plan.P, plan.S,
-                     plan.streamk ? " stream-K" : "", (long long)plan.grid);
+                     plan.streamk ? " stream-K" : (plan.persistent ? " persistent" : ""), (long long)plan.grid);
 
     hipError_t e;
     if (plan.general) {
@@ -533,6 +563,9 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
             sp.counters = reinterpret_cast<int *>(cnt);
             sp.units = plan.sk_units;
             e = c.sk[plan.P][epilogue](sp, (int)plan.grid, stream);
+        } else if (plan.persistent) {
+            p.C = C;
+            e = c.persist[epilogue](p, (int)plan.grid, stream);
         } else if (plan.S == 1) {
             p.C = C;
             e = c.fn[plan.P][epilogue](p, (int)plan.grid, stream);
@@ -737,6 +770,7 @@ int gemm_mkl_get_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, int
     out->workspace_bytes = plan.ws_bytes;
     out->streamk = plan.streamk ? 1 : 0;
     out->counter_bytes = (int32_t)plan.sk_counter_bytes;
+    out->persistent = plan.persistent ? 1 : 0;
     return GEMM_MKL_STATUS_OK;
 }
 

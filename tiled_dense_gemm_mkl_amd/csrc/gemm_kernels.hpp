@@ -241,6 +241,17 @@ __device__ __forceinline__ int xcd_remap(int wg, int grid)
     return (wg % kXcd) * per + wg / kXcd;
 }
 
+// Tile id (within one batch) -> (tm, tn): tiles rastered in groups of group_m
+// tile rows, column-major inside a group.
+__device__ __forceinline__ void raster(int tile, int tiles_m, int tiles_n, int group_m, int &tm, int &tn)
+{
+    const int width = group_m * tiles_n;
+    const int first_m = (tile / width) * group_m;
+    const int gsize = min(tiles_m - first_m, group_m);
+    tm = first_m + (tile % width) % gsize;
+    tn = (tile % width) / gsize;
+}
+
 // ------------------------------------------------------------------ the tiled kernel
 
 // LDS row layout of one chunk: RB bytes per row (64 or 128), split in 16-byte
@@ -473,6 +484,12 @@ struct TileCore {
     // count.
     // A load with valid == false reads nothing from memory and fills its LDS
     // block with zeros (it keeps the per-chunk load count uniform).
+    // RFL: the descriptors were set up under a branch (the persistent ring
+    // re-runs setup() only when its loads move to the next tile), where the
+    // compiler cannot keep them in scalar registers by itself; reading them
+    // back with readfirstlane does (the LDS-DMA loads take them from scalar
+    // registers).
+    template <bool RFL = false>
     __device__ __forceinline__ void issue_one(int chunk, int slot, int q, bool valid = true)
     {
         const int64_t kb = (int64_t)chunk * RB;   // byte offset of the chunk in a row
@@ -482,24 +499,33 @@ struct TileCore {
         if (q < A_LOADS) {
             const int j = q;
             const uint32_t v = (col_a[j] * 16 < rem) ? voff_a[j] : kOutOfRange;
+            const i32x4 r = RFL ? uniform4(rsrc_a) : rsrc_a;
             if ((j & 3) == 0)
-                dma16_set_m0(rsrc_a, sbase + (li * A_LOADS + j) * 1024, v, soff);
+                dma16_set_m0(r, sbase + (li * A_LOADS + j) * 1024, v, soff);
             else
-                dma16_same_m0(rsrc_a, j & 3, v, soff);
+                dma16_same_m0(r, j & 3, v, soff);
         } else {
             const int j = q - A_LOADS;
             const uint32_t v = (col_b[j] * 16 < rem) ? voff_b[j] : kOutOfRange;
+            const i32x4 r = RFL ? uniform4(rsrc_b) : rsrc_b;
             if ((j & 3) == 0)
-                dma16_set_m0(rsrc_b, sbase + BM * RB + (li * B_LOADS + j) * 1024, v, soff);
+                dma16_set_m0(r, sbase + BM * RB + (li * B_LOADS + j) * 1024, v, soff);
             else
-                dma16_same_m0(rsrc_b, j & 3, v, soff);
+                dma16_same_m0(r, j & 3, v, soff);
         }
     }
 
+    __device__ __forceinline__ static i32x4 uniform4(i32x4 x)
+    {
+        return i32x4{__builtin_amdgcn_readfirstlane(x[0]), __builtin_amdgcn_readfirstlane(x[1]),
+                     __builtin_amdgcn_readfirstlane(x[2]), __builtin_amdgcn_readfirstlane(x[3])};
+    }
+
+    template <bool RFL = false>
     __device__ __forceinline__ void issue(int chunk, int slot, bool valid = true)
     {
 #pragma unroll
-        for (int q = 0; q < LOADS; ++q) issue_one(chunk, slot, q, valid);
+        for (int q = 0; q < LOADS; ++q) issue_one<RFL>(chunk, slot, q, valid);
     }
 
     __device__ __forceinline__ void read_one(int slot, int ks, int buf, int r)
@@ -549,6 +575,113 @@ struct TileCore {
             for (int u = (NMF + LGAP - 1) / LGAP; u < LPK; ++u) {
                 const int q = ks * LPK + u;
                 if (q < LOADS) issue_one(load_chunk, fill, q, valid);
+            }
+        }
+    }
+
+    // Tile q of the [l][tile] order of a problem -> (batch, tile row, tile column).
+    __device__ __forceinline__ static void tile_of(const TileParams &p, int q, int &lq, int &tm, int &tn)
+    {
+        const int tiles = p.tiles_m * p.tiles_n;
+        lq = q / tiles;
+        raster(q % tiles, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    }
+
+    // The producer/consumer ring over the whole sequence of this workgroup's
+    // tiles (tiles w, w + G, w + 2G, ... of the [l][tile] order, ntiles of
+    // them), C = p.total_chunks chunks each: the ring's units are the
+    // (tile, chunk) pairs, tile-major, with the slots, waits and barriers of
+    // run(), so the first chunks of the next tile are loaded while the MFMA
+    // waves finish the current one.  After the barrier that ends a tile's last
+    // unit the MFMA waves stage the tile in `stage` (STAGE_BYTES of LDS beside
+    // the ring), every wave meets at one more barrier, and the MFMA waves
+    // store the staged tile while the producers go on loading.  The staging
+    // area is written again only after at least one more unit barrier, which
+    // every MFMA wave passes after its stores (hence its reads of the staged
+    // tile) have been issued.
+    template <int MODE>
+    __device__ void run_persistent(const TileParams &p, int w, int G, int ntiles, char *stage)
+    {
+        static_assert(NP > 0 && P >= 2 && WK == 1, "the persistent ring uses producer waves");
+        static_assert(MODE != MODE_PARTIAL, "the persistent grid does not split K");
+        const int C = p.total_chunks;
+        const int U = ntiles * C;
+        if (U <= 0) return;   // the same for every wave of the workgroup
+        if (!mma) {
+            // setup() runs only when the loads move on to the next tile: it
+            // costs a few hundred cycles, which must not delay every chunk's
+            // loads
+            int loaded = -1;   // tile (0 .. ntiles - 1) whose descriptors are set up
+            int lt = 0, lc = 0;   // tile and chunk of the next unit to load
+            int fill = 0;
+            for (int j = 0; j < P; ++j) {
+                if (lt != loaded && lt < ntiles) {
+                    int lq, tm, tn;
+                    tile_of(p, w + lt * G, lq, tm, tn);
+                    setup(p, lq, tm, tn);
+                    loaded = lt;
+                }
+                issue<true>(lc, fill, j < U);
+                ++fill;
+                if (++lc == C) {
+                    lc = 0;
+                    ++lt;
+                }
+            }
+            wait_vmcnt<LOADS * (P - 2)>();   // units 0 and 1 have landed
+            block_barrier();
+            int ci = 0;   // chunk of the unit being consumed
+            for (int i = 0; i < U; ++i) {
+                if (lt != loaded && lt < ntiles) {
+                    int lq, tm, tn;
+                    tile_of(p, w + lt * G, lq, tm, tn);
+                    setup(p, lq, tm, tn);
+                    loaded = lt;
+                }
+                issue<true>(lc, fill, i + P < U);
+                if (++lc == C) {
+                    lc = 0;
+                    ++lt;
+                }
+                wait_vmcnt<LOADS * (P - 2)>();
+                block_barrier();                       // end of unit i
+                if (++ci == C) {
+                    ci = 0;
+                    lds_barrier();                     // the tile of unit i is staged
+                }
+                fill = (fill + 1 == SLOTS) ? 0 : fill + 1;
+            }
+            wait_vmcnt<0>();
+        } else {
+            T *out = reinterpret_cast<T *>(p.C);
+            block_barrier();
+#pragma unroll
+            for (int ks = 0; ks < RA; ++ks)
+#pragma unroll
+                for (int r = 0; r < NRD; ++r) read_one(0, ks, ks % NB, r);
+            int slot = 0;
+            int cidx = 0, tile = 0;   // chunk and tile of unit i
+            for (int i = 0; i < U; ++i) {
+                if (cidx == 0) zero();
+                const int next = (slot + 1 == SLOTS) ? 0 : slot + 1;
+#pragma unroll
+                for (int ks = 0; ks < KSW; ++ks) step(ks, slot, next, 0, 0, false);
+                block_barrier();                       // end of unit i
+                if (cidx == C - 1) {
+                    int lq, tm, tn;
+                    tile_of(p, w + tile * G, lq, tm, tn);
+                    m0 = (int64_t)tm * BM;
+                    n0 = (int64_t)tn * BN;
+                    stage_tile<MODE, T>(stage);
+                    lds_barrier();                     // the tile is staged
+                    store_from_stage<MODE, T>(stage, out + (int64_t)lq * p.M * p.N, p.M, p.N, NWM * 64,
+                                              (int)threadIdx.x);
+                }
+                if (++cidx == C) {
+                    cidx = 0;
+                    ++tile;
+                }
+                slot = next;
             }
         }
     }
@@ -734,14 +867,26 @@ struct TileCore {
     template <int MODE, class OT>
     __device__ __forceinline__ void store_staged(OT *out, int64_t M, int64_t N)
     {
+        lds_barrier();   // every wave's ring reads and loads are done
+        stage_tile<MODE, OT>(smem);
+        lds_barrier();   // the whole tile is in LDS
+        store_from_stage<MODE, OT>(smem, out, M, N, THREADS, (int)threadIdx.x);
+    }
+
+    // Bytes of one finished tile in the staged layout (output type T).
+    static constexpr int STAGE_BYTES = BM * BN * (int)sizeof(T);
+
+    // The MFMA waves of k-group 0 write the finished tile (epilogue applied,
+    // converted to OT) to `stage`, row-major with each row's 16-byte columns
+    // XOR-swizzled by the row index.
+    template <int MODE, class OT>
+    __device__ __forceinline__ void stage_tile(char *stage)
+    {
         constexpr int OES = (int)sizeof(OT);
         constexpr int ROWB = BN * OES;          // bytes per tile row
         constexpr int NC = ROWB / 16;           // 16-byte columns per row
-        constexpr int EPC = 16 / OES;           // elements per 16-byte column
-        constexpr int RPP = THREADS / NC;       // rows per pass of the workgroup
         constexpr int GROUPS = MM::regs / 4;
-        static_assert(ROWB % 16 == 0 && THREADS % NC == 0, "staged store layout");
-        lds_barrier();   // every wave's ring reads and loads are done
+        static_assert(ROWB % 16 == 0, "staged store layout");
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             if (kg != 0 || !mma) break;   // (k-group 0 holds the sums)
@@ -758,7 +903,7 @@ struct TileCore {
                         y[q] = (MODE == MODE_PARTIAL) ? v : apply_epilogue<MODE>(v);
                     }
                     const int byte = cn * OES;
-                    char *dst = smem + r * ROWB + ((((byte >> 4) ^ (r % NC)) << 4) | (byte & 15));
+                    char *dst = stage + r * ROWB + ((((byte >> 4) ^ (r % NC)) << 4) | (byte & 15));
                     if constexpr (OES == 4)
                         *reinterpret_cast<f32x4v *>(dst) = f32x4v{y[0], y[1], y[2], y[3]};
                     else
@@ -766,13 +911,26 @@ struct TileCore {
                 }
             }
         }
-        lds_barrier();   // the whole tile is in LDS
-        const int t = threadIdx.x;
+    }
+
+    // Threads 0 .. nthreads - 1 store the staged tile at (m0, n0) of `out`
+    // ([M][N]) with one 16-byte access per lane, lanes running along rows, so
+    // that every store instruction writes whole cache lines instead of 8
+    // bytes in each of 32 rows.
+    template <int MODE, class OT>
+    __device__ __forceinline__ void store_from_stage(const char *stage, OT *out, int64_t M, int64_t N, int nthreads,
+                                                     int t)
+    {
+        constexpr int OES = (int)sizeof(OT);
+        constexpr int ROWB = BN * OES;
+        constexpr int NC = ROWB / 16;
+        constexpr int EPC = 16 / OES;           // elements per 16-byte column
+        const int rpp = nthreads / NC;          // rows per pass
         const int c = t % NC;
         const bool vec16 = ((N * OES) & 15) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
 #pragma unroll
-        for (int rr = t / NC; rr < BM; rr += RPP) {
-            const i32x4 v = *reinterpret_cast<const i32x4 *>(smem + rr * ROWB + ((c ^ (rr % NC)) << 4));
+        for (int rr = t / NC; rr < BM; rr += rpp) {
+            const i32x4 v = *reinterpret_cast<const i32x4 *>(stage + rr * ROWB + ((c ^ (rr % NC)) << 4));
             const int64_t gm = m0 + rr;
             const int64_t gn = n0 + c * EPC;
             if (gm >= M) continue;
@@ -899,16 +1057,6 @@ struct TileCore {
     }
 };
 
-// Tile id (within one batch) -> (tm, tn): tiles rastered in groups of group_m
-// tile rows, column-major inside a group.
-__device__ __forceinline__ void raster(int tile, int tiles_m, int tiles_n, int group_m, int &tm, int &tn)
-{
-    const int width = group_m * tiles_n;
-    const int first_m = (tile / width) * group_m;
-    const int gsize = min(tiles_m - first_m, group_m);
-    tm = first_m + (tile % width) % gsize;
-    tn = (tile % width) / gsize;
-}
 
 // Data-parallel / split-K grid: one workgroup per (batch, split, tile).
 template <class T, int BM, int BN, int RB, int WAVES_M, int WAVES_N, int MF, int P, int MODE, int WK = 1,
@@ -1048,6 +1196,26 @@ __global__ __launch_bounds__((WAVES_M *WAVES_N + NP) * 64) void gemm_grouped_ker
     c.zero();
     c.run(0, gp.total_chunks);
     c.template store<MODE>(p.C, rows, gp.N);
+}
+
+// Persistent grid (producer configurations, split 1): G = gridDim.x
+// workgroups, one per compute unit; workgroup w (after the XCD remap) takes
+// tiles w, w + G, w + 2G, ... of the [l][tile] order, so each round of G
+// concurrent tiles is a contiguous block of the raster, and one ring runs
+// across all of its tiles (TileCore::run_persistent).
+template <class T, int BM, int BN, int RB, int WAVES_M, int WAVES_N, int MF, int P, int MODE, int NP>
+__global__ __launch_bounds__((WAVES_M *WAVES_N + NP) * 64) void gemm_persistent_kernel(TileParams p)
+{
+    typedef TileCore<T, BM, BN, RB, WAVES_M, WAVES_N, MF, P, 1, NP> Core;
+    static_assert(Core::LDS_BYTES + Core::STAGE_BYTES <= 160 * 1024, "ring and staging area in LDS");
+    __shared__ __attribute__((aligned(1024))) char smem[Core::LDS_BYTES + Core::STAGE_BYTES];
+    Core c;
+    c.init(smem);
+    const int G = gridDim.x;
+    const int w = xcd_remap(blockIdx.x, G);
+    const int total = p.tiles_m * p.tiles_n * (int)p.L;
+    const int ntiles = w < total ? (total - w + G - 1) / G : 0;
+    c.template run_persistent<MODE>(p, w, G, ntiles, smem + Core::LDS_BYTES);
 }
 
 // ------------------------------------------------------------------ stream-K

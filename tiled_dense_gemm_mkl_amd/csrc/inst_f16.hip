@@ -23,8 +23,8 @@ void register_f16(std::vector<ConfigEntry> &t, DtypeKernels &k)
         make_entry<T, 128, 128, 128, 2, 2, 32, 0, 1, 2, 3>(d, 3, 0.4f, "f16 128x128 k64 waves2x2 mfma32")));
     // producer waves: NP extra waves issue every global->LDS load
     //                     T  BM   BN   RB  waves WK NP MF  prefetch depths
-    t.push_back(with_grouped<T, 128, 128, 128, 2, 2, 4, 32, 4>(
-        make_entry_kp<T, 128, 128, 128, 2, 2, 1, 4, 32, 2, 3, 4>(d, 4, 0.42f, "f16 128x128 k64 waves2x2+4p mfma32")));
+    t.push_back(with_persistent<T, 128, 128, 128, 2, 2, 4, 32, 3>(with_grouped<T, 128, 128, 128, 2, 2, 4, 32, 4>(
+        make_entry_kp<T, 128, 128, 128, 2, 2, 1, 4, 32, 2, 3, 4>(d, 4, 0.42f, "f16 128x128 k64 waves2x2+4p mfma32"))));
     t.push_back(make_entry_kp<T, 128, 128, 128, 2, 2, 1, 2, 32, 2, 3>(d, 3, 0.41f, "f16 128x128 k64 waves2x2+2p mfma32"));
     t.push_back(make_entry_kp<T, 128, 256, 128, 2, 2, 1, 4, 32, 2>(d, 2, 0.36f, "f16 128x256 k64 waves2x2+4p mfma32"));
     t.push_back(make_entry_kp<T, 256, 128, 128, 2, 2, 1, 4, 32, 2>(d, 2, 0.35f, "f16 256x128 k64 waves2x2+4p mfma32"));
