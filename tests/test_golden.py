@@ -35,3 +35,25 @@ def test_handworked_int_gemm(orc):
         assert np.array_equal(orc.gemm64(a, b, dtype, "identity"), C_id)
         got = orc.gemm64(a, b, dtype, "relu")
         assert np.array_equal(got, C_relu) and not np.any(np.signbit(got))
+
+
+def test_handworked_rms_norm(orc):
+    """RMSNorm against hand-worked closed forms (tests/golden/handworked_rms_norm.txt):
+    binary64 within 4 units in the last place, for every storage type (the
+    inputs are exact in all three)."""
+    with open(os.path.join(HERE, "golden", "handworked_rms_norm.txt")) as f:
+        lines = [l.split() for l in f if l.strip() and not l.startswith("#")]
+    i, cases = 0, 0
+    while i < len(lines):
+        assert lines[i][0] == "case"
+        rows, hidden, eps = int(lines[i][1]), int(lines[i][2]), float(lines[i][3])
+        x = np.array([[float(v) for v in lines[i + 1 + r]] for r in range(rows)])
+        w = np.array([float(v) for v in lines[i + 1 + rows]])
+        y = np.array([[float(v) for v in lines[i + 2 + rows + r]] for r in range(rows)])
+        assert x.shape == (rows, hidden) and w.shape == (hidden,) and y.shape == (rows, hidden)
+        for dtype in ("f32", "f16", "bf16"):
+            got = orc.rms_norm64(orc.round_to_dtype(x, dtype), orc.round_to_dtype(w, dtype), eps, dtype)
+            assert np.all(np.abs(got - y) <= 4 * 2.0 ** -52 * np.abs(y)), (dtype, got, y)
+        i += 2 + 2 * rows
+        cases += 1
+    assert cases == 5
