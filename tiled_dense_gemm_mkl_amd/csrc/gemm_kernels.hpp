@@ -604,6 +604,7 @@ struct TileCore {
     {
         static_assert(NP > 0 && P >= 2 && WK == 1, "the persistent ring uses producer waves");
         static_assert(MODE != MODE_PARTIAL, "the persistent grid does not split K");
+        static_assert((NWM * 64) % (BN * (int)sizeof(T) / 16) == 0, "MFMA threads store whole rows of the tile");
         const int C = p.total_chunks;
         const int U = ntiles * C;
         if (U <= 0) return;   // the same for every wave of the workgroup
@@ -867,6 +868,7 @@ struct TileCore {
     template <int MODE, class OT>
     __device__ __forceinline__ void store_staged(OT *out, int64_t M, int64_t N)
     {
+        static_assert(THREADS % (BN * (int)sizeof(OT) / 16) == 0, "every thread stores whole rows of 16-byte columns");
         lds_barrier();   // every wave's ring reads and loads are done
         stage_tile<MODE, OT>(smem);
         lds_barrier();   // the whole tile is in LDS
