@@ -27,6 +27,7 @@ using namespace gmk;
 namespace {
 
 constexpr int kNumCUs = 256;          // MI355X compute units (8 XCDs x 32)
+constexpr double kMallBytes = 256.0 * (1 << 20);   // memory-side (Infinity) cache
 constexpr int64_t kMaxSplit = 16;
 constexpr int64_t kMaxGroups = 65536;   // grouped GEMM: groups per call
 
@@ -148,7 +149,14 @@ double model_cycles(const ConfigEntry &c, int dtype, int64_t M, int64_t N, int64
     const int chunks = (total_chunks + S - 1) / S;
     const double bk = (double)c.rb / elem_bytes(dtype);
     const double peak = dtype == GEMM_MKL_F32 ? 256.0 : 4096.0;  // flop / clk / CU
-    const double eff = c.eff;
+    double eff = c.eff;
+    // Operands far larger than the 256 MB memory-side cache stream from HBM,
+    // whose latency a ring with a single chunk in flight does not cover.
+    // Measured: on the batched 512x3584x18944 bf16 shape (1.2 GB of
+    // operands) depth 1 with 64-wide chunks ran 4% slower than depth 4 with
+    // 32-wide chunks; on operands that fit the cache it ran 4% faster.
+    const double operand_bytes = (double)L * (double)(M + N) * (double)K * elem_bytes(dtype);
+    if (c.default_p <= 1 && operand_bytes > 2.0 * kMallBytes) eff *= 0.9;
     const double per_chunk = 2.0 * c.bm * c.bn * bk / (peak * eff) + 60.0;
     double cyc = (double)rounds * (chunks * per_chunk + 1500.0);
     if (S > 1) {
