@@ -1060,6 +1060,29 @@ struct TileCore {
 };
 
 
+// Tile of workgroup blockIdx.x for the data-parallel grid.  With many tiles
+// (two rounds of the chip or more, one batch, no split, a tile grid of even
+// rows and a multiple of 4 columns) the tile grid is cut into a 2 x 4 grid of
+// equal blocks, one per XCD (the hardware hands workgroup b to XCD b % 8), and
+// each XCD walks its block in the usual raster: an XCD then reads only its
+// block's rows of A and columns of B instead of every column of B (measured
+// on fp16 8192^3: 913 -> 892 us).  Otherwise `tile` (the id after the XCD
+// remap) is rastered over the whole grid.
+__device__ __forceinline__ void xcd_block_raster(const TileParams &p, int tile, int &tm, int &tn)
+{
+    const int tiles = p.tiles_m * p.tiles_n;
+    if (p.L == 1 && p.split == 1 && (p.tiles_m % 2) == 0 && (p.tiles_n % 4) == 0 && tiles >= 512) {
+        const int x = (int)(blockIdx.x % 8), loc = (int)(blockIdx.x / 8);
+        const int br = p.tiles_m / 2, bc = p.tiles_n / 4;
+        int r, c;
+        raster(loc, br, bc, p.group_m, r, c);
+        tm = (x / 4) * br + r;
+        tn = (x % 4) * bc + c;
+    } else {
+        raster(tile, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    }
+}
+
 // Data-parallel / split-K grid: one workgroup per (batch, split, tile).
 template <class T, int BM, int BN, int RB, int WAVES_M, int WAVES_N, int MF, int P, int MODE, int WK = 1,
           int NP = 0>
@@ -1078,7 +1101,7 @@ __global__ __launch_bounds__((WAVES_M *WAVES_N *WK + NP) * 64) void gemm_tile_ke
     const int s = t % p.split;
     const int l = t / p.split;
     int tm, tn;
-    raster(tile, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    xcd_block_raster(p, tile, tm, tn);
 
     const int chunk0 = s * p.chunks_per_split;
     int nk = p.total_chunks - chunk0;
