@@ -12,6 +12,11 @@ path (tiling, LDS-staged prefetch ring, MFMA mainloop, fused epilogue; plus the
 split-K reduction when the plan splits K).  Inputs are seeded synthetic
 operands resident in HBM before the timed region starts.
 
+The K timed steps are captured into one HIP graph on a stream of their own
+and replayed once (--no-graph launches them one by one from the host): the
+per-launch host and dispatch cost then stays out of the kernel times, as in a
+serving loop that replays captured work.
+
 Prints ONE JSON line with the metric, the roofline of the dominant kernel
 (measured with HIP events on the stream the kernels run on) and the CPU
 oracle timed on this host's cores.
@@ -65,6 +70,42 @@ def measured_traffic(workload_key: str, kernel: str, sources=None):
         return int(e["bytes_per_launch"])
     except (OSError, ValueError, KeyError, TypeError):
         return None
+
+
+def time_steps(step, steps: int, warmup: int, stream, graph: bool = False):
+    """Run `warmup` untimed steps, then time exactly `steps` steps on `stream`
+    (a synchronize on both sides of the region).  Returns (wall-clock ms per
+    step, ms per step from HIP events recorded on `stream`).  With graph=True
+    the `steps` calls are first captured into one HIP graph and the timed
+    region replays it, so the host issues one launch for all of them."""
+    import torch
+
+    torch.cuda.synchronize()   # inputs made on other streams are in place
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    g = None
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(steps):
+                step()
+        g.replay()   # one untimed replay
+        torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    if g is not None:
+        g.replay()
+    else:
+        for _ in range(steps):
+            step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall * 1e3 / steps, start.elapsed_time(end) / steps
 
 
 def cpu_baseline(w, A, B, budget_s: float = 10.0):
@@ -128,6 +169,7 @@ def cold_cache_rate(w, a, b, c, step_ptrs, steps: int) -> dict:
     nbytes = a.numel() * a.element_size() + b.numel() * b.element_size()
     copies = max(2, math.ceil((512 << 20) / nbytes) + 1)
     bufs = [(a.clone(), b.clone()) for _ in range(copies)]
+    torch.cuda.synchronize()
     ptrs = [(x.data_ptr(), y.data_ptr()) for x, y in bufs]
     for i in range(copies):
         step_ptrs(*ptrs[i])
@@ -178,7 +220,7 @@ def bench_grouped(args, key: str) -> int:
     o = torch.from_numpy(offs).to(dev)
     c = torch.empty((w.total_m, w.N), dtype=a.dtype, device=dev)
     dcode, ecode = gm.DTYPE_CODES[w.dtype], gm.EPILOGUE_CODES[w.epilogue]
-    stream = torch.cuda.current_stream(dev)
+    stream = torch.cuda.Stream(dev)   # a stream of its own (graph capture needs one)
     sptr = stream.cuda_stream
     ptrs = (a.data_ptr(), b.data_ptr(), c.data_ptr(), o.data_ptr())
     kernel = gm.config_names()[gm.grouped_config(w.G, w.total_m, w.N, w.K, dcode, ecode)] + " grouped"
@@ -188,20 +230,8 @@ def bench_grouped(args, key: str) -> int:
         if st != 0:
             raise gm.GemmMklError(st, gm.status_string(st))
 
-    for _ in range(args.warmup):
-        step()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    ev_ms = start.elapsed_time(end) / args.steps
+    with torch.cuda.stream(stream):
+        ms_per_step, ev_ms = time_steps(step, args.steps, args.warmup, stream, args.graph)
     peak = PEAK_TFLOPS[w.dtype]
     value = w.flops / (ms_per_step * 1e-3) / 1e12
     achieved = w.flops / (ev_ms * 1e-3) / 1e12
@@ -252,7 +282,7 @@ def bench_rms_norm(args, key: str) -> int:
     wt = workloads.storage_to_torch(W, w.dtype).to(dev)
     y = torch.empty_like(x)
     dcode = gm.DTYPE_CODES[w.dtype]
-    stream = torch.cuda.current_stream(dev)
+    stream = torch.cuda.Stream(dev)   # a stream of its own (graph capture needs one)
     sptr = stream.cuda_stream
     xp, wp, yp = x.data_ptr(), wt.data_ptr(), y.data_ptr()
     variant = gm.rms_norm_variant(w.rows, w.hidden, dcode, True)
@@ -263,20 +293,8 @@ def bench_rms_norm(args, key: str) -> int:
         if st != 0:
             raise gm.GemmMklError(st, gm.status_string(st))
 
-    for _ in range(args.warmup):
-        step()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    ev_ms = start.elapsed_time(end) / args.steps
+    with torch.cuda.stream(stream):
+        ms_per_step, ev_ms = time_steps(step, args.steps, args.warmup, stream, args.graph)
     nbytes = w.algorithmic_bytes
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (ev_ms * 1e-3) / 1e9
@@ -325,6 +343,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="launch every timed step from the host instead of replaying them from one HIP graph")
     ap.add_argument("--cold", action="store_true",
                     help="also time calls that rotate over copies of A and B larger than the caches")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -359,7 +379,7 @@ def main() -> int:
     dcode = gm.DTYPE_CODES[w.dtype]
     ecode = gm.EPILOGUE_CODES[w.epilogue]
     plan = gm.get_plan(w.M, w.N, w.K, w.L, dcode, ecode)
-    stream = torch.cuda.current_stream(dev)
+    stream = torch.cuda.Stream(dev)   # a stream of its own (graph capture needs one)
     sptr = stream.cuda_stream
     ap_, bp_, cp_ = a.data_ptr(), b.data_ptr(), c.data_ptr()
 
@@ -371,27 +391,13 @@ def main() -> int:
     def step():
         step_ptrs(ap_, bp_)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
     # HIP events on the stream the kernels run on bracket the K launches: the
     # launches queue back to back, so their span over K is the average launch
     # duration the roofline uses (rocprofv3's kernel trace of the same command
     # shows no idle gap between consecutive launches).  The wall clock over
     # the same region gives the throughput.
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    ev_ms_per_launch = start.elapsed_time(end) / args.steps
+    with torch.cuda.stream(stream):
+        ms_per_step, ev_ms_per_launch = time_steps(step, args.steps, args.warmup, stream, args.graph)
 
     value = w.flops / (ms_per_step * 1e-3) / 1e12
     achieved = w.flops / (ev_ms_per_launch * 1e-3) / 1e12
