@@ -281,6 +281,22 @@ int gemm_mkl_get_plan(int64_t M, int64_t N, int64_t K, int64_t L,
                       int dtype, int epilogue, const gemm_mkl_opts *opts,
                       gemm_mkl_plan *plan);
 
+/*
+ * The tile each workgroup of the plan's data-parallel (or split-K) grid
+ * computes, as the kernel derives it from its workgroup id: for workgroup b
+ * of the plan's grid, out[4b .. 4b+3] = (batch, K split, tile row, tile
+ * column).  The order shows the XCD-aware raster (workgroup b runs on XCD
+ * b % 8).  `out` is host memory of `capacity` int32 entries, owned by the
+ * caller; it must hold 4 * grid entries (gemm_mkl_get_plan gives the grid).
+ * Argument checks as in gemm_mkl_get_plan; NOT_AVAILABLE when the plan uses
+ * the general, stream-K or persistent kernel (no such per-workgroup tile),
+ * INVALID_VALUE when out is NULL or too small.  Empty problems write
+ * nothing.  Launches nothing.
+ */
+int gemm_mkl_tile_order(int64_t M, int64_t N, int64_t K, int64_t L,
+                        int dtype, int epilogue, const gemm_mkl_opts *opts,
+                        int32_t *out, int64_t capacity);
+
 /* Bytes of split-K workspace for the plan of these arguments (0 if none). */
 size_t gemm_mkl_workspace_size(int64_t M, int64_t N, int64_t K, int64_t L,
                                int dtype, int split_k);

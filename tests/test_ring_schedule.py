@@ -16,7 +16,8 @@ its program and meeting the others at each barrier, it checks:
   data  every MFMA consumes the fragments of its own (chunk, k-step).
 
 Planted mistakes in the schedule (a wait one too loose, a missing barrier, a
-ring slot off by one, a missing drain) must each be caught.
+ring slot off by one, a missing drain, the steady-state wait kept in the
+producers' tail where no zero fills follow) must each be caught.
 """
 
 import pytest
@@ -86,18 +87,28 @@ def schedule(KSW, NMF, NRD, LOADS, P, nk, producers=False, mut=None, tile_chunks
         ev.append(("wait", 0))
         return [ev], KSW * NMF, KSW * NRD
 
-    # producer waves load, MFMA waves read and compute
+    # producer waves load, MFMA waves read and compute.  The data-parallel
+    # producers load real chunks only and wait for exactly the loads that
+    # follow the chunk they need (wait_chunks_after); the persistent ring
+    # keeps one load count per unit with zero fills.
+    def tail_wait(j):
+        if mut == "steady_tail_wait":
+            return WAIT
+        return LOADS * max(0, min(j, P - 2)) + (mut == "loose_wait")
+
     prod, mma = [], []
     for c in range(P):
-        for q in range(LOADS):
-            prod.append(("load", c if c < nk else None, c))
-    prod.append(("wait", WAIT))
+        if tile_chunks or c < nk:
+            for q in range(LOADS):
+                prod.append(("load", c if c < nk else None, c))
+    prod.append(("wait", WAIT if tile_chunks else tail_wait(min(P, nk) - 2)))
     prod.append(("bar", False))
     fill = first_fill
     for i in range(nk):
-        for q in range(LOADS):
-            prod.append(("load", min(i + P, nk - 1) if i + P < nk else None, fill))
-        prod.append(("wait", WAIT))
+        if tile_chunks or i + P < nk:
+            for q in range(LOADS):
+                prod.append(("load", min(i + P, nk - 1) if i + P < nk else None, fill))
+        prod.append(("wait", WAIT if tile_chunks else tail_wait(min(i + P, nk - 1) - (i + 2))))
         if mut != "no_barrier":
             prod.append(("bar", False))
         if tile_chunks and i % tile_chunks == tile_chunks - 1 and mut != "no_stage_barrier":
@@ -282,6 +293,7 @@ def test_persistent_missing_stage_barrier_is_caught():
     ("no_barrier", False, 2), ("no_barrier", True, 3),
     ("slot_off", False, 3), ("slot_off", True, 2),
     ("no_drain", False, 1),
+    ("steady_tail_wait", True, 3), ("steady_tail_wait", True, 4),
 ])
 def test_planted_schedule_mistake_is_caught(mut, producers, P):
     caught = False

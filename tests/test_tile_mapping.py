@@ -51,3 +51,59 @@ def test_blocked_xcd_reads_one_block():
         rows = {m for m, _ in cells}
         cols = {n for _, n in cells}
         assert len(rows) == 16 and len(cols) == 8 and len(cells) == 128
+
+
+# ------------------------------------------------------------------ the library's own map
+
+import math  # noqa: E402
+
+import tiled_dense_gemm_mkl_amd as gm  # noqa: E402
+
+
+@pytest.mark.parametrize("M,N,K,L,dtype,split", [
+    (512, 5632, 2048, 1, "bf16", None),      # 176 tiles, one round
+    (8192, 8192, 8192, 1, "f16", None),      # blocked
+    (4096, 8192, 2048, 1, "bf16", None),     # blocked
+    (4096, 5632, 2048, 1, "bf16", None),
+    (512, 3584, 18944, 8, "bf16", None),     # batches
+    (700, 2200, 264, 3, "f16", None),        # ragged last raster group, batches
+    (1000, 1100, 520, 1, "f32", None),
+    (128, 2048, 2048, 1, "f32", None),
+    (300, 5000, 4096, 2, "bf16", 3),         # forced K split with batches
+    (2000, 2100, 1000, 2, "bf16", 2),
+    (96, 80, 18944, 1, "bf16", 7),
+    (1, 1, 8, 1, "bf16", None),
+    (4224, 4352, 64, 1, "f16", None),        # blocked, group rows past the block
+])
+def test_library_map_matches_the_model(M, N, K, L, dtype, split):
+    """gemm_mkl_tile_order runs the kernel's own map (multiply-high divisions,
+    built by the host) for every workgroup of the planned grid; it must equal
+    the model above, written with plain integer division."""
+    code = gm.DTYPE_CODES[dtype]
+    opts = gm.make_opts(split_k=split) if split else None
+    plan = gm.get_plan(M, N, K, L, code, gm.EPI_RELU, opts)
+    if plan["general"] or plan["streamk"] or plan["persistent"]:
+        with pytest.raises(gm.GemmMklError):
+            gm.tile_order(M, N, K, L, code, gm.EPI_RELU, opts)
+        return
+    tiles_m, tiles_n = math.ceil(M / plan["block_m"]), math.ceil(N / plan["block_n"])
+    S, grid = plan["split_k"], plan["grid"]
+    assert grid == tiles_m * tiles_n * L * S
+    got = gm.tile_order(M, N, K, L, code, gm.EPI_RELU, opts)
+    want = [tile_of(b, grid, tiles_m, tiles_n, L, S, min(4, tiles_m)) for b in range(grid)]
+    assert got.shape == (grid, 4)
+    assert [tuple(r) for r in got.tolist()] == want
+
+
+def test_library_map_refuses_short_output_and_other_grids():
+    code = gm.BF16
+    with pytest.raises(gm.GemmMklError):
+        gm.tile_order(8192, 8192, 64, 1, code, gm.EPI_RELU, gm.make_opts(force_general=True))
+    lib = gm.load()
+    import numpy as np
+    out = np.zeros(4 * 175, np.int32)
+    assert lib.gemm_mkl_tile_order(512, 5632, 2048, 1, code, gm.EPI_RELU, None, out.ctypes.data, out.size) == -1
+    assert lib.gemm_mkl_tile_order(512, 5632, 2048, 1, code, gm.EPI_RELU, None, None, 4 * 176) == -1
+    out = np.zeros(4 * 176, np.int32)
+    assert lib.gemm_mkl_tile_order(512, 5632, 2048, 1, code, gm.EPI_RELU, None, out.ctypes.data, out.size) == 0
+    assert lib.gemm_mkl_tile_order(0, 5632, 2048, 1, code, gm.EPI_RELU, None, None, 0) == 0

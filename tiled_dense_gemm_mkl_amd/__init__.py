@@ -29,6 +29,7 @@ from ._binding import (  # noqa: F401
     gemm_mkl_grouped,
     gemm_mkl_rms_norm,
     get_plan,
+    tile_order,
     grouped_config,
     load,
     make_opts,

@@ -80,6 +80,7 @@ EXPORTS = (
     "gemm_mkl_grouped_config",
     "gemm_mkl_opts_init",
     "gemm_mkl_get_plan",
+    "gemm_mkl_tile_order",
     "gemm_mkl_workspace_size",
     "gemm_mkl_release_workspace",
     "gemm_mkl_status_string",
@@ -119,6 +120,8 @@ def load(path: str = LIB_PATH):
     lib.gemm_mkl_opts_init.restype = None
     lib.gemm_mkl_get_plan.argtypes = [i64, i64, i64, i64, i32, i32, ctypes.POINTER(Opts), ctypes.POINTER(Plan)]
     lib.gemm_mkl_get_plan.restype = i32
+    lib.gemm_mkl_tile_order.argtypes = [i64, i64, i64, i64, i32, i32, ctypes.POINTER(Opts), ctypes.c_void_p, i64]
+    lib.gemm_mkl_tile_order.restype = i32
     lib.gemm_mkl_workspace_size.argtypes = [i64, i64, i64, i64, i32, i32]
     lib.gemm_mkl_workspace_size.restype = ctypes.c_size_t
     lib.gemm_mkl_release_workspace.argtypes = []
@@ -229,6 +232,21 @@ def get_plan(M, N, K, L, dtype, epilogue, opts: Opts | None = None) -> dict:
     if st != 0:
         raise GemmMklError(st, status_string(st))
     return p.as_dict()
+
+
+def tile_order(M, N, K, L, dtype, epilogue, opts: Opts | None = None):
+    """int32 array [grid, 4]: (batch, K split, tile row, tile column) of each
+    workgroup of the plan's data-parallel grid, in workgroup order."""
+    import numpy as np
+
+    grid = get_plan(M, N, K, L, dtype, epilogue, opts)["grid"]
+    out = np.zeros((max(grid, 0), 4), dtype=np.int32)
+    st = load().gemm_mkl_tile_order(M, N, K, L, dtype, epilogue,
+                                    ctypes.byref(opts) if opts is not None else None,
+                                    out.ctypes.data, out.size)
+    if st != 0:
+        raise GemmMklError(st, status_string(st))
+    return out
 
 
 def workspace_size(M, N, K, L, dtype, split_k=0) -> int:

@@ -552,6 +552,7 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
         p.split = plan.S;
         p.chunks_per_split = plan.chunks_per_split;
         p.total_chunks = plan.total_chunks;
+        p.map = make_tile_map(plan.tiles_m, plan.tiles_n, (int)L, plan.S, plan.group_m, (int)plan.grid);
         if (plan.streamk) {
             p.C = C;
             void *ws = nullptr, *cnt = nullptr;
@@ -779,6 +780,29 @@ int gemm_mkl_get_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, int
     out->streamk = plan.streamk ? 1 : 0;
     out->counter_bytes = (int32_t)plan.sk_counter_bytes;
     out->persistent = plan.persistent ? 1 : 0;
+    return GEMM_MKL_STATUS_OK;
+}
+
+int gemm_mkl_tile_order(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, int epilogue,
+                        const gemm_mkl_opts *opts, int32_t *out, int64_t capacity)
+{
+    int st = check_args(M, N, K, L, dtype, epilogue, opts);
+    if (st != GEMM_MKL_STATUS_OK) return st;
+    if (M == 0 || N == 0 || L == 0) return GEMM_MKL_STATUS_OK;
+    Plan plan;
+    st = cached_plan(M, N, K, L, dtype, opts, true, &plan);
+    if (st != GEMM_MKL_STATUS_OK) return st;
+    if (plan.general || plan.streamk || plan.persistent) return GEMM_MKL_STATUS_NOT_AVAILABLE;
+    if (!out || capacity < 4 * plan.grid) return GEMM_MKL_STATUS_INVALID_VALUE;
+    const TileMap m = make_tile_map(plan.tiles_m, plan.tiles_n, (int)L, plan.S, plan.group_m, (int)plan.grid);
+    for (int64_t b = 0; b < plan.grid; ++b) {
+        int l, s, tm, tn;
+        map_workgroup(m, (uint32_t)b, l, s, tm, tn);
+        out[4 * b] = l;
+        out[4 * b + 1] = s;
+        out[4 * b + 2] = tm;
+        out[4 * b + 3] = tn;
+    }
     return GEMM_MKL_STATUS_OK;
 }
 

@@ -53,6 +53,111 @@ enum Mode { MODE_IDENTITY = 0, MODE_RELU = 1, MODE_SILU = 2, MODE_PARTIAL = 3 };
 // A voffset at or above every buffer's num_records: the load returns zeros.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
+// n / d for 32-bit unsigned n and 1 <= d < 2^31 by one multiply-high and two
+// shifts: division by an invariant integer (Granlund and Montgomery,
+// "Division by Invariant Integers using Multiplication", PLDI 1994, section
+// 4).  With l = ceil(log2 d) and mul = floor(2^32 (2^l - d) / d) + 1:
+//   t = (mul * n) >> 32,   n / d = (t + ((n - t) >> sh1)) >> sh2,
+// sh1 = min(l, 1), sh2 = max(l - 1, 0) (d = 1 gives mul = 1, t = 0).  On the
+// GPU every step of it is a scalar instruction, where a plain division goes
+// through the vector unit's float reciprocal and back.
+struct FastDiv {
+    uint32_t mul, sh1, sh2;
+};
+
+inline FastDiv make_fastdiv(uint32_t d)
+{
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    FastDiv f;
+    f.mul = (uint32_t)(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+    f.sh1 = l < 1 ? l : 1;
+    f.sh2 = l > 1 ? l - 1 : 0;
+    return f;
+}
+
+__host__ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f)
+{
+    const uint32_t t = (uint32_t)(((uint64_t)f.mul * n) >> 32);
+    return (t + ((n - t) >> f.sh1)) >> f.sh2;
+}
+
+// Workgroup -> (batch, split, tile row, tile column) of the data-parallel
+// grid, every division precomputed by the host (make_tile_map).
+//   - Hardware dispatches consecutive workgroup ids round-robin over the 8
+//     XCDs.  The full rounds are renumbered so that each XCD holds a
+//     contiguous range of ids (the ragged last round keeps its ids); the id
+//     is then split [batch][split][tile].
+//   - Blocked grids (one batch, no split, an even number of tile rows, tile
+//     columns a multiple of 4, at least 512 tiles): XCD x = id % 8 walks
+//     block (x / 4, x % 4) of a 2 x 4 cut of the tile grid, so that it reads
+//     only that block's rows of A and columns of B instead of every column
+//     of B (measured on fp16 8192^3: 913 -> 892 us).
+//   - Tiles are rastered, over the grid or the block, in groups of `group`
+//     tile rows, column-major inside a group (tiles sharing B columns run
+//     together and share the L2).
+struct TileMap {
+    int32_t per;                  // full rounds of the 8 XCDs: grid / 8
+    int32_t tiles, split;         // tiles of one batch; K splits
+    FastDiv d_tiles, d_split;
+    int32_t blocked;
+    int32_t rows, cols;           // the rastered area: the grid, or one block
+    int32_t group, last_first;    // tile rows per group; first row of the last group
+    FastDiv d_width, d_group, d_last;   // by group * cols, group, rows of the last group
+};
+
+// (row, column) of tile `tile` of the rastered area.
+__host__ __device__ __forceinline__ void raster_map(const TileMap &m, uint32_t tile, int &r, int &c)
+{
+    const uint32_t gi = fdiv(tile, m.d_width);
+    const int first = (int)gi * m.group;
+    const bool last = first >= m.last_first;
+    const int gsize = last ? m.rows - first : m.group;
+    const uint32_t u = tile - gi * (uint32_t)(m.group * m.cols);
+    const uint32_t q = fdiv(u, last ? m.d_last : m.d_group);
+    r = first + (int)(u - q * (uint32_t)gsize);
+    c = (int)q;
+}
+
+// Branch-free, so that the compiler loads every field in one round of kernel
+// argument loads.  In a blocked grid the id within the XCD's block,
+// b / 8 < tiles, gives batch and split 0 by the same divisions.
+__host__ __device__ __forceinline__ void map_workgroup(const TileMap &m, uint32_t b, int &l, int &s, int &tm,
+                                                       int &tn)
+{
+    const uint32_t per = (uint32_t)m.per;
+    const uint32_t remapped = b < 8u * per ? (b & 7) * per + (b >> 3) : b;
+    const uint32_t t = m.blocked ? (b >> 3) : remapped;
+    const uint32_t q = fdiv(t, m.d_tiles);
+    const uint32_t lq = fdiv(q, m.d_split);
+    l = (int)lq;
+    s = (int)(q - lq * (uint32_t)m.split);
+    raster_map(m, t - q * (uint32_t)m.tiles, tm, tn);
+    tm += m.blocked ? (int)((b & 7) >> 2) * m.rows : 0;
+    tn += m.blocked ? (int)(b & 3) * m.cols : 0;
+}
+
+// The map of a grid of `grid` workgroups over L batches, `split` K splits and
+// tiles_m x tiles_n tiles, rastered in groups of group_m tile rows.
+inline TileMap make_tile_map(int tiles_m, int tiles_n, int L, int split, int group_m, int grid)
+{
+    TileMap m;
+    m.per = grid / 8;
+    m.tiles = tiles_m * tiles_n;
+    m.split = split;
+    m.d_tiles = make_fastdiv((uint32_t)m.tiles);
+    m.d_split = make_fastdiv((uint32_t)split);
+    m.blocked = (L == 1 && split == 1 && tiles_m % 2 == 0 && tiles_n % 4 == 0 && m.tiles >= 512) ? 1 : 0;
+    m.rows = m.blocked ? tiles_m / 2 : tiles_m;
+    m.cols = m.blocked ? tiles_n / 4 : tiles_n;
+    m.group = group_m < 1 ? 1 : (group_m > m.rows ? m.rows : group_m);
+    m.last_first = (m.rows - 1) / m.group * m.group;
+    m.d_width = make_fastdiv((uint32_t)(m.group * m.cols));
+    m.d_group = make_fastdiv((uint32_t)m.group);
+    m.d_last = make_fastdiv((uint32_t)(m.rows - m.last_first));
+    return m;
+}
+
 struct TileParams {
     const void *A;
     const void *B;
@@ -63,6 +168,7 @@ struct TileParams {
     int32_t split;            // S
     int32_t chunks_per_split; // K chunks per split (the last split may be short)
     int32_t total_chunks;     // ceil(K * elem / row bytes of a chunk)
+    TileMap map;              // the data-parallel grid's workgroup -> tile map
 };
 
 // ------------------------------------------------------------------ epilogue
@@ -528,6 +634,22 @@ struct TileCore {
         for (int q = 0; q < LOADS; ++q) issue_one<RFL>(chunk, slot, q, valid);
     }
 
+    // Wait until at most j chunks' loads of this wave (j clamped to
+    // [0, J]) are still in flight: the chunk issued just before those has
+    // landed.  j is uniform; vmcnt takes only immediates, hence the ladder.
+    template <int J>
+    __device__ __forceinline__ void wait_chunks_after(int j)
+    {
+        if constexpr (J <= 0) {
+            wait_vmcnt<0>();
+        } else {
+            if (j >= J)
+                wait_vmcnt<LOADS * J>();
+            else
+                wait_chunks_after<J - 1>(j);
+        }
+    }
+
     __device__ __forceinline__ void read_one(int slot, int ks, int buf, int r)
     {
         const char *base = smem + slot * SLOT_BYTES;
@@ -689,10 +811,12 @@ struct TileCore {
 
     // acc += sum over chunks [c_begin, c_begin + nk) of the tile.  On entry no
     // load of this workgroup is in flight; on exit none is, and every wave is
-    // past its last LDS read of the range.
+    // past its last LDS read of the range.  FRESH: the workgroup's first use
+    // of the slots (nothing can still be reading them).
+    template <bool FRESH = false>
     __device__ void run(int c_begin, int nk)
     {
-        lds_barrier();   // the slots may still be read by a previous range
+        if constexpr (!FRESH) lds_barrier();   // the slots may still be read by a previous range
         if constexpr (P == 0) {
             for (int i = 0; i < nk; ++i) {
                 if (i > 0) lds_barrier();   // everyone is done reading the single slot
@@ -715,14 +839,19 @@ struct TileCore {
             // chunk i + 2 has landed and meet the MFMA waves at the barrier
             // that ends chunk i.
             if (!mma) {
+                // Only real chunks are loaded (no zero fills past the last
+                // one: the MFMA waves' reads past the end are never used), so
+                // near the end fewer loads follow the chunk waited for.
 #pragma unroll
-                for (int c = 0; c < P; ++c) issue(c_begin + min(c, nk - 1), c, c < nk);
-                wait_vmcnt<LOADS * (P - 2)>();   // chunks 0 and 1 have landed
+                for (int c = 0; c < P; ++c)
+                    if (c < nk) issue(c_begin + c, c);
+                wait_chunks_after<P - 2>(min(P, nk) - 2);   // chunks 0 and 1 have landed
                 block_barrier();
                 int fill = P;
                 for (int i = 0; i < nk; ++i) {
-                    issue(c_begin + min(i + P, nk - 1), fill, i + P < nk);
-                    wait_vmcnt<LOADS * (P - 2)>();
+                    if (i + P < nk) issue(c_begin + i + P, fill);
+                    // chunk i + 2 has landed (chunks up to i + P were issued)
+                    wait_chunks_after<P - 2>(min(i + P, nk - 1) - (i + 2));
                     block_barrier();
                     fill = (fill + 1 == SLOTS) ? 0 : fill + 1;
                 }
@@ -1060,29 +1189,6 @@ struct TileCore {
 };
 
 
-// Tile of workgroup blockIdx.x for the data-parallel grid.  With many tiles
-// (two rounds of the chip or more, one batch, no split, a tile grid of even
-// rows and a multiple of 4 columns) the tile grid is cut into a 2 x 4 grid of
-// equal blocks, one per XCD (the hardware hands workgroup b to XCD b % 8), and
-// each XCD walks its block in the usual raster: an XCD then reads only its
-// block's rows of A and columns of B instead of every column of B (measured
-// on fp16 8192^3: 913 -> 892 us).  Otherwise `tile` (the id after the XCD
-// remap) is rastered over the whole grid.
-__device__ __forceinline__ void xcd_block_raster(const TileParams &p, int tile, int &tm, int &tn)
-{
-    const int tiles = p.tiles_m * p.tiles_n;
-    if (p.L == 1 && p.split == 1 && (p.tiles_m % 2) == 0 && (p.tiles_n % 4) == 0 && tiles >= 512) {
-        const int x = (int)(blockIdx.x % 8), loc = (int)(blockIdx.x / 8);
-        const int br = p.tiles_m / 2, bc = p.tiles_n / 4;
-        int r, c;
-        raster(loc, br, bc, p.group_m, r, c);
-        tm = (x / 4) * br + r;
-        tn = (x % 4) * bc + c;
-    } else {
-        raster(tile, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
-    }
-}
-
 // Data-parallel / split-K grid: one workgroup per (batch, split, tile).
 template <class T, int BM, int BN, int RB, int WAVES_M, int WAVES_N, int MF, int P, int MODE, int WK = 1,
           int NP = 0>
@@ -1093,15 +1199,16 @@ __global__ __launch_bounds__((WAVES_M *WAVES_N *WK + NP) * 64) void gemm_tile_ke
     Core c;
     c.init(smem);
 
-    // [l][s][tile], after the XCD remap
-    int t = xcd_remap(blockIdx.x, gridDim.x);
-    const int tiles = p.tiles_m * p.tiles_n;
-    const int tile = t % tiles;
-    t /= tiles;
-    const int s = t % p.split;
-    const int l = t / p.split;
-    int tm, tn;
-    xcd_block_raster(p, tile, tm, tn);
+    // The operand pointers and sizes in scalar registers before the first
+    // branch: every kernel argument then arrives in one round of loads (the
+    // compiler would otherwise sink some of them past the early return).
+    asm volatile("" : : "s"(p.A), "s"(p.B), "s"(p.C), "s"(p.M), "s"(p.N), "s"(p.K), "s"(p.L),
+                 "s"(p.chunks_per_split), "s"(p.total_chunks));
+    int l, s, tm, tn;
+    map_workgroup(p.map, blockIdx.x, l, s, tm, tn);
+    // (the host's map covers exactly the grid; a workgroup outside it would
+    // address memory past the operands)
+    if (l >= p.L || s >= p.split || tm >= p.tiles_m || tn >= p.tiles_n) return;
 
     const int chunk0 = s * p.chunks_per_split;
     int nk = p.total_chunks - chunk0;
@@ -1110,7 +1217,7 @@ __global__ __launch_bounds__((WAVES_M *WAVES_N *WK + NP) * 64) void gemm_tile_ke
 
     c.setup(p, l, tm, tn);
     c.zero();
-    c.run(chunk0, nk);
+    c.template run<true>(chunk0, nk);
     if constexpr (MODE == MODE_PARTIAL)
         c.template store<MODE>(reinterpret_cast<float *>(p.C) + ((int64_t)s * p.L + l) * p.M * p.N, p.M, p.N);
     else
@@ -1219,7 +1326,7 @@ __global__ __launch_bounds__((WAVES_M *WAVES_N + NP) * 64) void gemm_grouped_ker
     p.L = 1;
     c.setup(p, 0, tm, (int)tn);
     c.zero();
-    c.run(0, gp.total_chunks);
+    c.template run<true>(0, gp.total_chunks);
     c.template store<MODE>(p.C, rows, gp.N);
 }
 
