@@ -33,7 +33,7 @@ def schedule(KSW, NMF, NRD, LOADS, P, nk, producers=False, mut=None, tile_chunks
     NB = RA + 1
     SLOTS = P + 1
     WIN = KSW - RA
-    SPREAD = KSW if P >= 2 else WIN
+    SPREAD = KSW if P >= 2 else 1
     LPK = -(-LOADS // SPREAD)
     WAIT = LOADS * (P - 2) if P >= 2 else 0
     if mut == "loose_wait":
