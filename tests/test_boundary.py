@@ -380,3 +380,39 @@ def test_persistent_forced_where_unavailable(lib):
     with pytest.raises(gm.GemmMklError) as e:
         gm.get_plan(1024, 1024, 512, 1, BF16, ID, o)
     assert e.value.status == -1
+
+
+def test_planning_from_many_threads_matches_serial_planning():
+    """The plan cache is shared by all threads: plans made by 8 threads at
+    once (cache misses and hits interleaved) equal the plans a fresh process
+    makes one by one."""
+    import json
+    import subprocess
+    import sys
+    import threading
+
+    shapes = [(m, n, k, l, dt) for m in (1, 97, 513, 1001) for n in (65, 2049, 5633) for k in (8, 528, 2056)
+              for l in (1, 3) for dt in (gm.F32, gm.F16, gm.BF16)]
+    got, errors = {}, []
+
+    def worker(part):
+        try:
+            for s in part:
+                got[s] = gm.get_plan(*s, gm.EPI_RELU)
+        except Exception as e:
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(shapes[i::8] + shapes[(i + 1) % 8::8],)) for i in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors
+    code = ("import json, sys; import tiled_dense_gemm_mkl_amd as gm; "
+            "shapes = json.loads(sys.stdin.read()); "
+            "print(json.dumps([gm.get_plan(*s, gm.EPI_RELU) for s in shapes]))")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], input=json.dumps(shapes), capture_output=True, text=True,
+                       cwd=root, timeout=120, check=True)
+    serial = json.loads(r.stdout)
+    assert [got[s] for s in shapes] == serial
