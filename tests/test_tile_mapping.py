@@ -1,8 +1,9 @@
 """CPU model of the data-parallel grid's workgroup -> tile mapping
-(gemm_tile_kernel and xcd_block_raster in
-tiled_dense_gemm_mkl_amd/csrc/gemm_kernels.hpp): every (batch, split, tile)
-is covered exactly once, and with the XCD blocking each XCD (workgroup b runs
-on XCD b % 8) covers one contiguous block of the tile grid."""
+(TileMap / map_workgroup in tiled_dense_gemm_mkl_amd/csrc/gemm_kernels.hpp),
+written with plain integer division: every (batch, split, tile) is covered
+exactly once, and with the XCD blocking each XCD (workgroup b runs on XCD
+b % 8) covers one contiguous block of the tile grid.  The library's own map
+(multiply-high divisions, gemm_mkl_tile_order) must equal the model."""
 import pytest
 
 from test_grouped_mapping import raster, xcd_remap
