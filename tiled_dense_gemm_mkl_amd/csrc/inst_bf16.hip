@@ -35,7 +35,10 @@ void register_bf16(std::vector<ConfigEntry> &t, DtypeKernels &k)
     t.push_back(make_entry_k<T, 128, 128, 128, 1, 2, 2, 32, 2, 3>(d, 3, 0.4f, "bf16 128x128 k64 waves1x2x2 mfma32"));
     t.push_back(make_entry_k<T, 128, 128, 128, 2, 2, 2, 32, 2, 3>(d, 3, 0.4f, "bf16 128x128 k64 waves2x2x2 mfma32"));
     t.push_back(with_grouped<T, 64, 64, 128, 2, 2, 0, 32, 2>(
-        make_entry<T, 64, 64, 128, 2, 2, 32, 1, 2, 3>(d, 2, 0.22f, "bf16 64x64 k64 waves2x2 mfma32")));
+        // one wave per SIMD: depth 3 covers the memory latency that depth 2
+        // leaves exposed (bf16 1024x1024x4096 34.9 -> 20.4 us, 128x5632x2048
+        // 12.0 -> 9.5 us, 512x2048x2048 12.2 -> 9.8 us)
+        make_entry<T, 64, 64, 128, 2, 2, 32, 1, 2, 3>(d, 3, 0.22f, "bf16 64x64 k64 waves2x2 mfma32")));
     t.push_back(make_entry<T, 128, 128, 128, 2, 2, 16, 2>(d, 2, 0.3f, "bf16 128x128 k64 waves2x2 mfma16"));
     t.push_back(make_entry<T, 256, 256, 128, 2, 2, 16, 1>(d, 1, 0.4f, "bf16 256x256 k64 waves2x2 mfma16"));
     t.push_back(make_entry<T, 256, 256, 128, 2, 4, 16, 1>(d, 1, 0.40f, "bf16 256x256 k64 waves2x4 mfma16"));
