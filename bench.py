@@ -353,7 +353,7 @@ def main() -> int:
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
-              "the GEMM is not sharded across GPUs in this build", file=sys.stderr)
+              "the library runs each GEMM on a single GPU and has no multi-GPU path", file=sys.stderr)
         return 2
     if args.calibrate_copy:
         return copy_calibration(args.calibrate_copy, max(1, args.steps))
