@@ -21,9 +21,14 @@
  *
  * Pointers: A, B, C are DEVICE pointers owned by the caller; the library never
  * allocates, frees or retains them.  C must not overlap A or B.  Each base
- * pointer must be aligned to its element size; 16-byte aligned pointers with
- * K*sizeof(element) a multiple of 16 take the fast kernels, anything else a
- * slower general kernel (same results up to fp32 summation order).
+ * pointer must be aligned to its element size.  The tile kernels read A and B
+ * in 16-byte pieces: when K*sizeof(element) is not a multiple of 16, or A or
+ * B is not 16-byte aligned, the call first copies the operand(s) into rows of
+ * Kp elements (K rounded up to 16 bytes, zero-filled past K) in the workspace
+ * and runs the tile kernels on those (plan.packed = 1; the zeros add nothing,
+ * so the result is that of the tile kernels at the padded K).  A C that is
+ * not aligned to 4 elements, or GEMM_MKL_OPT_FORCE_GENERAL, takes a slower
+ * general kernel instead (same results up to fp32 summation order).
  *
  * Stream: `stream` is a hipStream_t (NULL = the default stream).  Calls only
  * enqueue work and return without synchronising; a kernel fault surfaces at
@@ -122,9 +127,12 @@ int gemm_mkl(const void *A, const void *B, void *C,
  *   faster than the data-parallel grid); GEMM_MKL_PERSISTENT=-1 lets the plan
  *   take it whenever there are more tiles than compute units, =1 always.
  * workspace / workspace_bytes: caller-owned device memory for split-K or
- *   stream-K partial sums (NULL = use the library's internal workspace).  It
- *   must hold the plan's workspace_bytes (gemm_mkl_get_plan) and be 256-byte
- *   aligned; too small is GEMM_MKL_STATUS_WORKSPACE.  A stream-K plan uses its
+ *   stream-K partial sums and repacked operands (NULL = use the library's
+ *   internal workspace).  It must hold the plan's workspace_bytes
+ *   (gemm_mkl_get_plan, which assumes 16-byte aligned pointers: a misaligned
+ *   A or B also needs its repacked copy, L * rows * Kp * element bytes
+ *   rounded up to 256) and be 256-byte aligned; too small is
+ *   GEMM_MKL_STATUS_WORKSPACE, before anything is launched.  A stream-K plan uses its
  *   first plan.counter_bytes bytes as per-tile counters: they must be zero
  *   before the first stream-K call with that workspace, and every completed
  *   call leaves them zero.
@@ -274,7 +282,9 @@ typedef struct gemm_mkl_plan {
     int32_t streamk;          /* 1 if the stream-K kernel is used (grid = workgroups) */
     int32_t counter_bytes;    /* stream-K: leading workspace bytes holding counters */
     int32_t persistent;       /* 1 if the persistent grid is used (grid = workgroups) */
-    int32_t reserved;
+    int32_t packed;           /* 1 if A and B are first copied into zero-padded,
+                                 16-byte aligned rows in the workspace (K * elem
+                                 not a multiple of 16 bytes) */
 } gemm_mkl_plan;
 
 int gemm_mkl_get_plan(int64_t M, int64_t N, int64_t K, int64_t L,

@@ -162,14 +162,41 @@ def test_plans_of_the_workloads(lib, key):
     assert gm.workspace_size(w.M, w.N, w.K, w.L, code, 2) == p2["workspace_bytes"]
 
 
-def test_unaligned_K_takes_the_general_kernel(lib):
-    p = gm.get_plan(33, 17, 13, 2, BF16, RELU)     # K * 2 bytes is not a multiple of 16
-    assert p["general"] == 1 and p["split_k"] == 1
-    p = gm.get_plan(33, 17, 16, 2, BF16, RELU)
-    assert p["general"] == 0
-    with pytest.raises(gm.GemmMklError) as e:      # a split cannot be forced on it
-        gm.get_plan(33, 17, 13, 2, BF16, RELU, gm.make_opts(split_k=2))
-    assert e.value.status == -6
+def _round256(n):
+    return (n + 255) // 256 * 256
+
+
+def test_unaligned_K_is_repacked(lib):
+    """K * element size not a multiple of 16: A and B are copied into rows of
+    Kp elements (K rounded up to 16 bytes) in the workspace, and the plan is
+    the aligned plan at Kp; the general kernel runs only when forced."""
+    M, N, K, L = 33, 17, 13, 2
+    p = gm.get_plan(M, N, K, L, BF16, RELU)          # 26-byte rows
+    want = gm.get_plan(M, N, 16, L, BF16, RELU)      # the same call at Kp = 16
+    assert p["general"] == 0 and p["packed"] == 1 and want["packed"] == 0
+    for key in ("config_id", "prefetch_stages", "split_k", "grid", "block_m", "block_n"):
+        assert p[key] == want[key], key
+    assert p["workspace_bytes"] == _round256(L * M * 16 * 2) + _round256(L * N * 16 * 2)
+    # a forced split: partials first, then the two packed operands
+    K2, Kp2 = 1001, 1008
+    p2 = gm.get_plan(M, N, K2, L, BF16, RELU, gm.make_opts(split_k=2))
+    assert p2["split_k"] == 2 and p2["packed"] == 1
+    assert p2["workspace_bytes"] == (_round256(2 * L * M * N * 4) + _round256(L * M * Kp2 * 2)
+                                     + _round256(L * N * Kp2 * 2))
+    assert gm.workspace_size(M, N, K2, L, BF16, 2) == p2["workspace_bytes"]
+    # fp32: rows padded to a multiple of 4 elements
+    p3 = gm.get_plan(70, 65, 37, 1, F32, RELU)
+    assert p3["packed"] == 1 and p3["workspace_bytes"] == _round256(70 * 40 * 4) + _round256(65 * 40 * 4)
+    # the general kernel when forced; stream-K and the persistent grid are not
+    # offered on repacked operands
+    g = gm.get_plan(M, N, K, L, BF16, RELU, gm.make_opts(force_general=True))
+    assert g["general"] == 1 and g["packed"] == 0 and g["workspace_bytes"] == 0
+    for opts in (gm.make_opts(streamk=True), gm.make_opts(persistent=True)):
+        with pytest.raises(gm.GemmMklError) as e:
+            gm.get_plan(M, N, K, L, BF16, RELU, opts)
+        assert e.value.status == -6
+    # aligned K is not repacked
+    assert gm.get_plan(M, N, 16, L, BF16, RELU)["packed"] == 0
 
 
 def test_every_prefetch_depth_of_a_config_is_plannable(lib):

@@ -57,16 +57,20 @@ def test_ragged_shapes_all_epilogues(orc, dtype, shape):
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("shape", [(33, 17, 13, 2), (70, 65, 37, 1), (5, 129, 3, 3), (64, 64, 1, 1)],
                          ids=lambda s: "x".join(map(str, s)))
-def test_general_kernel_unaligned_K(orc, dtype, shape):
+def test_unaligned_K_repacked_and_general(orc, dtype, shape):
+    """Rows that are not a multiple of 16 bytes: the automatic plan repacks A
+    and B; the general kernel (forced) must agree with the oracle as well."""
     M, N, K, L = shape
     A, B = _operands(dtype, M, N, K, L, seed=K + 1)
     plan = gm.get_plan(M, N, K, L, gm.DTYPE_CODES[dtype], gm.EPI_RELU)
     if (K * (4 if dtype == "f32" else 2)) % 16:
-        assert plan["general"] == 1
+        assert plan["packed"] == 1 and plan["general"] == 0
     for epi in EPIS:
         ref = orc.gemm64(A, B, dtype, epi)
         C = run_gemm(A, B, dtype, epi)
-        assert_close(C, ref, A, B, dtype, K, f"general {dtype} {shape} {epi}")
+        assert_close(C, ref, A, B, dtype, K, f"repacked {dtype} {shape} {epi}")
+        Cg = run_gemm(A, B, dtype, epi, force_general=True)
+        assert_close(Cg, ref, A, B, dtype, K, f"general {dtype} {shape} {epi}")
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -78,7 +82,7 @@ def test_general_kernel_forced_and_misaligned(orc, dtype):
     ref = orc.gemm64(A, B, dtype, "silu")
     C = run_gemm(A, B, dtype, "silu", force_general=True)
     assert_close(C, ref, A, B, dtype, K, "forced general")
-    # operands that start one element past a 16-byte boundary take the general kernel
+    # operands that start one element past a 16-byte boundary are repacked
     a_big = to_device(np.concatenate([A.reshape(-1)[:1], A.reshape(-1)]), dtype)
     b_big = to_device(np.concatenate([B.reshape(-1)[:1], B.reshape(-1)]), dtype)
     a = a_big[1:].view(L, M, K)

@@ -66,7 +66,7 @@ class Plan(ctypes.Structure):
         ("streamk", ctypes.c_int32),
         ("counter_bytes", ctypes.c_int32),
         ("persistent", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("packed", ctypes.c_int32),
     ]
 
     def as_dict(self) -> dict:

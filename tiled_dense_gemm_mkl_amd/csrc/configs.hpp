@@ -20,6 +20,8 @@ typedef hipError_t (*GroupedLaunchFn)(const GroupedParams &p, int grid, hipStrea
 typedef hipError_t (*ReduceLaunchFn)(const float *W, void *C, int64_t total, int split, hipStream_t stream);
 typedef hipError_t (*GeneralLaunchFn)(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
                                       int64_t L, hipStream_t stream);
+typedef hipError_t (*PackLaunchFn)(const void *src, void *dst, int64_t rows, int64_t K, int64_t Kp,
+                                   hipStream_t stream);
 
 struct ConfigEntry {
     int dtype;             // GEMM_MKL_F32 / F16 / BF16
@@ -43,6 +45,7 @@ struct ConfigEntry {
 struct DtypeKernels {
     ReduceLaunchFn reduce[3];    // by epilogue
     GeneralLaunchFn general[3];  // by epilogue
+    PackLaunchFn pack;           // operand rows into 16-byte aligned, zero-padded rows
 };
 
 // Filled by the instantiation units (one per dtype).
@@ -197,8 +200,19 @@ hipError_t launch_general(const void *A, const void *B, void *C, int64_t M, int6
 }
 
 template <class T>
+hipError_t launch_pack(const void *src, void *dst, int64_t rows, int64_t K, int64_t Kp, hipStream_t stream)
+{
+    const int64_t blocks = rows < 65536 ? rows : 65536;
+    if (blocks < 1) return hipSuccess;
+    hipLaunchKernelGGL((pack_rows_kernel<T>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const T *>(src), reinterpret_cast<T *>(dst), rows, K, Kp);
+    return hipGetLastError();
+}
+
+template <class T>
 void fill_dtype_kernels(DtypeKernels &k)
 {
+    k.pack = &launch_pack<T>;
     k.reduce[0] = &launch_reduce<T, MODE_IDENTITY>;
     k.reduce[1] = &launch_reduce<T, MODE_RELU>;
     k.reduce[2] = &launch_reduce<T, MODE_SILU>;

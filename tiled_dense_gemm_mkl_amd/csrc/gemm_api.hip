@@ -106,6 +106,19 @@ struct Plan {
     int32_t tiles_m = 0, tiles_n = 0, group_m = 1;
     int32_t total_chunks = 0, chunks_per_split = 0;
     size_t ws_bytes = 0;
+    // operands repacked into zero-padded, 16-byte aligned rows of Kp elements
+    // in the workspace (after the split-K partials) before the tile kernel
+    bool packed = false, pack_a = false, pack_b = false;
+    int64_t Kp = 0;
+    size_t off_a = 0, off_b = 0;
+};
+
+// Alignment of a call's operands, as the planner sees it.
+enum : int {
+    kAlignA = 1,     // A 16-byte aligned
+    kAlignB = 2,     // B 16-byte aligned
+    kAlignC = 4,     // C aligned to 4 elements
+    kAlignAll = 7,
 };
 
 int check_args(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, int epilogue, const gemm_mkl_opts *o)
@@ -215,7 +228,7 @@ double model_streamk_cycles(const ConfigEntry &c, int dtype, int64_t M, int64_t 
     return cyc;
 }
 
-int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_mkl_opts *o, bool ptrs_aligned,
+int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_mkl_opts *o, int align,
               Plan *plan)
 {
     Registry &R = registry();
@@ -254,7 +267,48 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
 
     if ((K * es + 63) / 64 > INT32_MAX) return GEMM_MKL_STATUS_NOT_AVAILABLE;
 
-    bool general = force_general || !ptrs_aligned;
+    // Operands whose rows (K elements) or base pointers are not 16-byte
+    // aligned are first copied into zero-padded, aligned rows in the
+    // workspace, and the call is then planned like an aligned one at the
+    // padded K (the zeros add nothing to any sum).  C is stored as it is.
+    const bool rows_ok = (K * es) % 16 == 0;
+    if (!force_general && (align & kAlignC) && K > 0 &&
+        (!rows_ok || !(align & kAlignA) || !(align & kAlignB))) {
+        if (sk_mode == 1 || pers_mode == 1) return GEMM_MKL_STATUS_NOT_AVAILABLE;
+        const int64_t vec = 16 / es;
+        const int64_t Kp = rows_ok ? K : (K + vec - 1) / vec * vec;
+        gemm_mkl_opts inner;
+        if (o)
+            inner = *o;
+        else
+            gemm_mkl_opts_init(&inner);
+        inner.flags = (inner.flags & ~(GEMM_MKL_OPT_STREAMK | GEMM_MKL_OPT_PERSISTENT)) | GEMM_MKL_OPT_NO_STREAMK |
+                      GEMM_MKL_OPT_NO_PERSISTENT;
+        Plan fast;
+        const int st = make_plan(M, N, Kp, L, dtype, &inner, kAlignAll, &fast);
+        if (st != GEMM_MKL_STATUS_OK) return st;
+        if (!fast.general) {
+            *plan = fast;
+            plan->packed = true;
+            plan->Kp = Kp;
+            plan->pack_a = !rows_ok || !(align & kAlignA);
+            plan->pack_b = !rows_ok || !(align & kAlignB);
+            size_t off = (plan->ws_bytes + 255) / 256 * 256;
+            if (plan->pack_a) {
+                plan->off_a = off;
+                off += ((size_t)(L * M * Kp * es) + 255) / 256 * 256;
+            }
+            if (plan->pack_b) {
+                plan->off_b = off;
+                off += ((size_t)(L * N * Kp * es) + 255) / 256 * 256;
+            }
+            plan->ws_bytes = off;
+            return GEMM_MKL_STATUS_OK;
+        }
+        // (a K too long for every tile configuration: the general kernel below)
+    }
+
+    bool general = force_general || align != kAlignAll;
     if (!general) {
         if (forced_cfg >= 0) {
             if (!fast_path_ok(R.table[forced_cfg], dtype, K)) general = true;
@@ -388,7 +442,7 @@ std::mutex g_plan_mutex;
 std::map<PlanKey, std::pair<int, Plan>> g_plans;
 constexpr size_t kMaxCachedPlans = 4096;
 
-int cached_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_mkl_opts *o, bool aligned,
+int cached_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_mkl_opts *o, int align,
                 Plan *plan)
 {
     PlanKey key;
@@ -398,7 +452,7 @@ int cached_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gem
     key.K = K;
     key.L = L;
     key.dtype = dtype;
-    key.aligned = aligned ? 1 : 0;
+    key.aligned = align;
     key.config_id = o ? o->config_id : -1;
     key.prefetch = o ? o->prefetch_stages : -1;
     key.split = o ? o->split_k : 0;
@@ -412,7 +466,7 @@ int cached_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gem
         }
     }
     Plan fresh;
-    const int st = make_plan(M, N, K, L, dtype, o, aligned, &fresh);
+    const int st = make_plan(M, N, K, L, dtype, o, align, &fresh);
     std::lock_guard<std::mutex> g(g_plan_mutex);
     if (g_plans.size() >= kMaxCachedPlans) g_plans.clear();
     g_plans.emplace(key, std::make_pair(st, fresh));
@@ -520,19 +574,20 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
     const int es = elem_bytes(dtype);
     auto al = [](const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; };
     if (!al(A, es) || !al(B, es) || !al(C, es)) return GEMM_MKL_STATUS_INVALID_VALUE;
-    const bool aligned = al(A, 16) && al(B, 16) && al(C, 4 * es);
+    const int align = (al(A, 16) ? kAlignA : 0) | (al(B, 16) ? kAlignB : 0) | (al(C, 4 * es) ? kAlignC : 0);
 
     Plan plan;
-    st = cached_plan(M, N, K, L, dtype, o, aligned, &plan);
+    st = cached_plan(M, N, K, L, dtype, o, align, &plan);
     if (st != GEMM_MKL_STATUS_OK) return st;
 
     Registry &R = registry();
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
     if (env().log)
-        std::fprintf(stderr, "gemm_mkl: M=%lld N=%lld K=%lld L=%lld dtype=%d epi=%d -> %s P=%d S=%d%s grid=%lld\n",
+        std::fprintf(stderr, "gemm_mkl: M=%lld N=%lld K=%lld L=%lld dtype=%d epi=%d -> %s P=%d S=%d%s%s grid=%lld\n",
                      (long long)M, (long long)N, (long long)K, (long long)L, dtype, epilogue,
                      plan.general ? "general" : R.table[plan.config_id].name, plan.P, plan.S,
-                     plan.streamk ? " stream-K" : (plan.persistent ? " persistent" : ""), (long long)plan.grid);
+                     plan.streamk ? " stream-K" : (plan.persistent ? " persistent" : ""),
+                     plan.packed ? " packed" : "", (long long)plan.grid);
 
     hipError_t e;
     if (plan.general) {
@@ -553,6 +608,34 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
         p.chunks_per_split = plan.chunks_per_split;
         p.total_chunks = plan.total_chunks;
         p.map = make_tile_map(plan.tiles_m, plan.tiles_n, (int)L, plan.S, plan.group_m, (int)plan.grid);
+        // the workspace of split-K partials (from offset 0) and repacked operands
+        void *ws = nullptr;
+        if (!plan.streamk && plan.ws_bytes > 0) {
+            if (o && o->workspace) {
+                if (o->workspace_bytes < plan.ws_bytes) return GEMM_MKL_STATUS_WORKSPACE;
+                ws = o->workspace;
+            } else {
+                st = get_workspace(stream, plan.ws_bytes, &ws);
+                if (st != GEMM_MKL_STATUS_OK) return st;
+            }
+        }
+        if (plan.packed) {
+            char *w = static_cast<char *>(ws);
+            e = hipSuccess;
+            if (plan.pack_a) {
+                e = R.k[dtype].pack(A, w + plan.off_a, L * M, K, plan.Kp, stream);
+                p.A = w + plan.off_a;
+            }
+            if (e == hipSuccess && plan.pack_b) {
+                e = R.k[dtype].pack(B, w + plan.off_b, L * N, K, plan.Kp, stream);
+                p.B = w + plan.off_b;
+            }
+            if (e != hipSuccess) {
+                t_last_hip = e;
+                return GEMM_MKL_STATUS_HIP_ERROR;
+            }
+            p.K = plan.Kp;
+        }
         if (plan.streamk) {
             p.C = C;
             void *ws = nullptr, *cnt = nullptr;
@@ -579,14 +662,6 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
             p.C = C;
             e = c.fn[plan.P][epilogue](p, (int)plan.grid, stream);
         } else {
-            void *ws = nullptr;
-            if (o && o->workspace) {
-                if (o->workspace_bytes < plan.ws_bytes) return GEMM_MKL_STATUS_WORKSPACE;
-                ws = o->workspace;
-            } else {
-                st = get_workspace(stream, plan.ws_bytes, &ws);
-                if (st != GEMM_MKL_STATUS_OK) return st;
-            }
             p.C = ws;
             e = c.fn[plan.P][MODE_PARTIAL](p, (int)plan.grid, stream);
             if (e == hipSuccess)
@@ -757,7 +832,7 @@ int gemm_mkl_get_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, int
         return GEMM_MKL_STATUS_OK;
     }
     Plan plan;
-    st = cached_plan(M, N, K, L, dtype, opts, true, &plan);
+    st = cached_plan(M, N, K, L, dtype, opts, kAlignAll, &plan);
     if (st != GEMM_MKL_STATUS_OK) return st;
     out->config_id = plan.config_id;
     out->prefetch_stages = plan.P;
@@ -780,6 +855,7 @@ int gemm_mkl_get_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, int
     out->streamk = plan.streamk ? 1 : 0;
     out->counter_bytes = (int32_t)plan.sk_counter_bytes;
     out->persistent = plan.persistent ? 1 : 0;
+    out->packed = plan.packed ? 1 : 0;
     return GEMM_MKL_STATUS_OK;
 }
 
@@ -790,7 +866,7 @@ int gemm_mkl_tile_order(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, i
     if (st != GEMM_MKL_STATUS_OK) return st;
     if (M == 0 || N == 0 || L == 0) return GEMM_MKL_STATUS_OK;
     Plan plan;
-    st = cached_plan(M, N, K, L, dtype, opts, true, &plan);
+    st = cached_plan(M, N, K, L, dtype, opts, kAlignAll, &plan);
     if (st != GEMM_MKL_STATUS_OK) return st;
     if (plan.general || plan.streamk || plan.persistent) return GEMM_MKL_STATUS_NOT_AVAILABLE;
     if (!out || capacity < 4 * plan.grid) return GEMM_MKL_STATUS_INVALID_VALUE;

@@ -1486,6 +1486,36 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
     }
 }
 
+// ------------------------------------------------------------------ row repacking
+
+// dst[r][k] = src[r][k] for k < K and 0 for K <= k < Kp, r < rows: copies
+// operand rows of any element alignment (a row length or base pointer that is
+// not a multiple of 16 bytes) into rows of Kp elements, Kp * sizeof(T) a
+// multiple of 16, at a 16-byte aligned dst, so that the tile kernels' 16-byte
+// loads apply.  The zeros past K add nothing to any dot product.  One
+// workgroup per row (grid-stride), one 16-byte vector of dst per thread;
+// element loads from src (bounds-checked by k < K), 16-byte stores.
+template <class T>
+__global__ __launch_bounds__(256) void pack_rows_kernel(const T *__restrict__ src, T *__restrict__ dst,
+                                                        int64_t rows, int64_t K, int64_t Kp)
+{
+    constexpr int V = 16 / (int)sizeof(T);   // elements per 16-byte vector
+    const int64_t vpr = Kp / V;               // vectors per dst row
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        const T *s = src + r * K;
+        T *d = dst + r * Kp;
+        for (int64_t v = threadIdx.x; v < vpr; v += 256) {
+            const int64_t k0 = v * V;
+            T e[V];
+#pragma unroll
+            for (int q = 0; q < V; ++q) e[q] = (k0 + q < K) ? s[k0 + q] : T(0.0f);
+            i32x4 w;
+            __builtin_memcpy(&w, e, 16);
+            *reinterpret_cast<i32x4 *>(d + k0) = w;
+        }
+    }
+}
+
 // ------------------------------------------------------------------ general kernel
 
 // Any alignment, any K: element-wise bounds-checked loads into LDS (as fp32),
