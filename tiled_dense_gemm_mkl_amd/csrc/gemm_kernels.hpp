@@ -1493,24 +1493,59 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 // not a multiple of 16 bytes) into rows of Kp elements, Kp * sizeof(T) a
 // multiple of 16, at a 16-byte aligned dst, so that the tile kernels' 16-byte
 // loads apply.  The zeros past K add nothing to any dot product.  One
-// workgroup per row (grid-stride), one 16-byte vector of dst per thread;
-// element loads from src (bounds-checked by k < K), 16-byte stores.
+// workgroup per row (grid-stride), one 16-byte piece of dst per thread.
+// A row starts `lead` bytes (0, or 2 for a 16-bit row) past a 4-byte
+// boundary: each piece is read as 20 bytes from that boundary (a 16-byte and
+// a 4-byte buffer load, dword-aligned) and shifted into place with
+// v_alignbyte.  A load that reaches past the operand's last byte would come
+// back zeroed by the buffer's range check, valid bytes included, so the
+// pieces whose 20 bytes do not all lie in the operand (the last one or two of
+// the last row) are read element by element instead.  The 4-byte word a row
+// starts in lies in the operand's allocation.
 template <class T>
 __global__ __launch_bounds__(256) void pack_rows_kernel(const T *__restrict__ src, T *__restrict__ dst,
                                                         int64_t rows, int64_t K, int64_t Kp)
 {
-    constexpr int V = 16 / (int)sizeof(T);   // elements per 16-byte vector
-    const int64_t vpr = Kp / V;               // vectors per dst row
+    constexpr int V = 16 / (int)sizeof(T);   // elements per 16-byte piece
+    const int64_t vpr = Kp / V;               // pieces per dst row
+    const uintptr_t end = reinterpret_cast<uintptr_t>(src + rows * K);
     for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
-        const T *s = src + r * K;
+        const uintptr_t row0 = reinterpret_cast<uintptr_t>(src + r * K);
+        const uintptr_t base = row0 & ~(uintptr_t)3;
+        const uint32_t lead = (uint32_t)(row0 - base);
+        const uint64_t avail = end - base;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            reinterpret_cast<void *>(base), (short)0, (int)(avail < 0x7fffffffu ? avail : 0x7fffffffu), 0x00020000);
         T *d = dst + r * Kp;
+        const T *s = src + r * K;
         for (int64_t v = threadIdx.x; v < vpr; v += 256) {
+            const int off = (int)(v * 16);
             const int64_t k0 = v * V;
-            T e[V];
-#pragma unroll
-            for (int q = 0; q < V; ++q) e[q] = (k0 + q < K) ? s[k0 + q] : T(0.0f);
             i32x4 w;
-            __builtin_memcpy(&w, e, 16);
+            if ((uint64_t)off + 20 <= avail) {
+                const i32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+                const int hi = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 16, 0, 0);
+                w = lo;
+                if (lead != 0) {
+                    w[0] = (int)__builtin_amdgcn_alignbyte((unsigned)lo[1], (unsigned)lo[0], lead);
+                    w[1] = (int)__builtin_amdgcn_alignbyte((unsigned)lo[2], (unsigned)lo[1], lead);
+                    w[2] = (int)__builtin_amdgcn_alignbyte((unsigned)lo[3], (unsigned)lo[2], lead);
+                    w[3] = (int)__builtin_amdgcn_alignbyte((unsigned)hi, (unsigned)lo[3], lead);
+                }
+            } else {
+                T e[V];
+#pragma unroll
+                for (int q = 0; q < V; ++q) e[q] = (k0 + q < K) ? s[k0 + q] : T(0.0f);
+                __builtin_memcpy(&w, e, 16);
+            }
+            if (k0 + V > K) {   // the row's last piece: zeros past K
+                T e[V];
+                __builtin_memcpy(e, &w, 16);
+#pragma unroll
+                for (int q = 0; q < V; ++q)
+                    if (k0 + q >= K) e[q] = T(0.0f);
+                __builtin_memcpy(&w, e, 16);
+            }
             *reinterpret_cast<i32x4 *>(d + k0) = w;
         }
     }
