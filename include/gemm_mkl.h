@@ -201,10 +201,16 @@ int gemm_mkl_ex(const void *A, const void *B, void *C,
  *   configuration that has grouped kernels (see gemm_mkl_config_name) and its
  *   depth; split_k > 1 or any flag is NOT_AVAILABLE (groups are never split).
  *
+ * Rows of K elements that are not a multiple of 16 bytes, or an A or B off a
+ * 16-byte boundary, are first copied into zero-padded rows of Kp elements (K
+ * rounded up to 16 bytes) in the workspace: opts->workspace, which must then
+ * hold the copies (A: total_m * Kp, B: G * N * Kp elements, each rounded up
+ * to 256 bytes, A first), or the library's internal one.
+ *
  * Returns GEMM_MKL_STATUS_OK (also for G, total_m or N equal to 0: no
  * launch), INVALID_VALUE (negative sizes, G > 65536, total_m >= 2^31, null or
- * element-misaligned pointers), UNSUPPORTED_DTYPE / _EPILOGUE, NOT_AVAILABLE
- * (A or B not 16-byte aligned, K * element size not a multiple of 16, or no
+ * element-misaligned pointers), UNSUPPORTED_DTYPE / _EPILOGUE, WORKSPACE (a
+ * caller workspace too small for the repacked operands), NOT_AVAILABLE (no
  * configuration fits) or HIP_ERROR.  Ownership as for gemm_mkl.
  */
 int gemm_mkl_grouped(const void *A, const void *B, void *C, const int32_t *offs,

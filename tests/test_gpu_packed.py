@@ -115,3 +115,39 @@ def test_caller_workspace_must_hold_the_repacked_operands(orc):
         else:
             assert_close(workloads.torch_to_storage(c), orc.gemm64(A, B, dtype, "relu"), A, B, dtype, K,
                          "caller workspace")
+
+
+# ------------------------------------------------------------------ grouped GEMM
+
+def _grouped_run(A, B, offs, dtype, epilogue, shift_a=False):
+    import torch
+
+    a = to_device(A, dtype)
+    if shift_a:   # the same values one element past a 16-byte boundary
+        big = to_device(np.concatenate([A.reshape(-1)[:1], A.reshape(-1)]), dtype)
+        a = big[1:].view(A.shape)
+    b = to_device(B, dtype)
+    o = torch.from_numpy(np.ascontiguousarray(offs, dtype=np.int32)).cuda()
+    c = gm.gemm_grouped(a, b, o, epilogue)
+    torch.cuda.synchronize()
+    return workloads.torch_to_storage(c)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("K,shift_a", [(1001, False), (13, False), (96, True)], ids=["K1001", "K13", "shiftedA"])
+def test_grouped_repacked(orc, dtype, K, shift_a):
+    """Grouped calls with rows that are not a multiple of 16 bytes, or an A
+    off a 16-byte boundary: against the oracle, and bit for bit against the
+    same call on host-padded operands."""
+    G, total_m, N = 5, 700, 300
+    offs = np.array([90, 90, 333, 600, 700], dtype=np.int32)   # one empty group
+    A, _ = workloads.random_operands(dtype, total_m, 1, K, 1, seed=K)
+    _, B = workloads.random_operands(dtype, 1, N, K, G, seed=K + 1)
+    A = A[0]
+    C = _grouped_run(A, B, offs, dtype, "relu", shift_a)
+    ref = orc.gemm_grouped64(A, B, offs, dtype, "relu")
+    assert_close(C, ref, A, B, dtype, K, f"grouped {dtype} K={K} shift_a={shift_a}")
+    vec = 16 // EB[dtype]
+    Kp = (K + vec - 1) // vec * vec
+    Cpad = _grouped_run(_pad(A, Kp), _pad(B, Kp), offs, dtype, "relu")
+    assert_bits_equal(C, Cpad, f"grouped {dtype} K={K} against host-padded")

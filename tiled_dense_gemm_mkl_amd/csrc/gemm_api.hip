@@ -728,10 +728,17 @@ int run_grouped(const void *A, const void *B, void *C, const int32_t *offs, int6
     if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_MKL_STATUS_INVALID_VALUE;
     auto al = [](const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; };
     if (!al(A, es) || !al(B, es) || !al(C, es) || !al(offs, 4)) return GEMM_MKL_STATUS_INVALID_VALUE;
-    // the tiled kernels only: 16-byte aligned operands and rows
-    if (!al(A, 16) || !al(B, 16) || (K * es) % 16 != 0) return GEMM_MKL_STATUS_NOT_AVAILABLE;
+    // The tiled kernels read 16-byte pieces: rows of K elements that are not
+    // a multiple of 16 bytes, or an A or B off a 16-byte boundary, are first
+    // copied into zero-padded rows of Kp elements in the workspace (the zeros
+    // add nothing to any sum).
+    const bool rows_ok = (K * es) % 16 == 0;
+    const bool pack_a = K > 0 && (!rows_ok || !al(A, 16));
+    const bool pack_b = K > 0 && (!rows_ok || !al(B, 16));
+    const int64_t vec = 16 / es;
+    const int64_t Kp = rows_ok ? K : (K + vec - 1) / vec * vec;
 
-    const int best = grouped_config(G, total_m, N, K, dtype, epilogue, o);
+    const int best = grouped_config(G, total_m, N, Kp, dtype, epilogue, o);
     if (best < 0) return best == -1 ? GEMM_MKL_STATUS_NOT_AVAILABLE : best;
     Registry &R = registry();
     const ConfigEntry &c = R.table[best];
@@ -743,20 +750,47 @@ int run_grouped(const void *A, const void *B, void *C, const int32_t *offs, int6
     gp.G = (int32_t)G;
     gp.total_m = (int32_t)total_m;
     gp.N = N;
-    gp.K = K;
+    gp.K = Kp;
     const int64_t tiles_n = (N + c.bn - 1) / c.bn;
     const int64_t row_tiles = (total_m + c.bm - 1) / c.bm + G;   // each group adds at most one partial tile
     const int64_t grid = row_tiles * tiles_n;
     if (tiles_n > INT32_MAX || row_tiles > INT32_MAX || grid > INT32_MAX) return GEMM_MKL_STATUS_NOT_AVAILABLE;
     gp.tiles_n = (int32_t)tiles_n;
     gp.row_tiles = (int32_t)row_tiles;
-    gp.total_chunks = (int32_t)((K * es + c.rb - 1) / c.rb);
+    gp.total_chunks = (int32_t)((Kp * es + c.rb - 1) / c.rb);
     gp.group_m = std::max<int32_t>(1, (int32_t)env().group_m);
     if (env().log)
         std::fprintf(stderr, "gemm_mkl_grouped: G=%lld rows=%lld N=%lld K=%lld dtype=%d epi=%d -> %s P=%d grid=%lld\n",
                      (long long)G, (long long)total_m, (long long)N, (long long)K, dtype, epilogue, c.name,
                      c.grouped_p, (long long)grid);
-    hipError_t e = c.grouped[epilogue](gp, (int)grid, reinterpret_cast<hipStream_t>(stream_v));
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+    if (pack_a || pack_b) {
+        const size_t bytes_a = pack_a ? ((size_t)(total_m * Kp * es) + 255) / 256 * 256 : 0;
+        const size_t need = bytes_a + (pack_b ? ((size_t)(G * N * Kp * es) + 255) / 256 * 256 : 0);
+        void *ws = nullptr;
+        if (o && o->workspace) {
+            if (o->workspace_bytes < need) return GEMM_MKL_STATUS_WORKSPACE;
+            ws = o->workspace;
+        } else {
+            const int st = get_workspace(stream, need, &ws);
+            if (st != GEMM_MKL_STATUS_OK) return st;
+        }
+        char *w = static_cast<char *>(ws);
+        hipError_t e = hipSuccess;
+        if (pack_a) {
+            e = R.k[dtype].pack(A, w, total_m, K, Kp, stream);
+            gp.A = w;
+        }
+        if (e == hipSuccess && pack_b) {
+            e = R.k[dtype].pack(B, w + bytes_a, G * N, K, Kp, stream);
+            gp.B = w + bytes_a;
+        }
+        if (e != hipSuccess) {
+            t_last_hip = e;
+            return GEMM_MKL_STATUS_HIP_ERROR;
+        }
+    }
+    hipError_t e = c.grouped[epilogue](gp, (int)grid, stream);
     if (e != hipSuccess) {
         t_last_hip = e;
         return GEMM_MKL_STATUS_HIP_ERROR;
@@ -814,8 +848,9 @@ int gemm_mkl_grouped_config(int64_t G, int64_t total_m, int64_t N, int64_t K, in
         if (opts->prefetch_stages < -1 || opts->split_k < 0 || opts->config_id < -1) return GEMM_MKL_STATUS_INVALID_VALUE;
         if (opts->flags != 0 || opts->split_k > 1) return GEMM_MKL_STATUS_NOT_AVAILABLE;
     }
-    if ((K * elem_bytes(dtype)) % 16 != 0) return GEMM_MKL_STATUS_NOT_AVAILABLE;
-    const int id = grouped_config(G, total_m, N, K, dtype, epilogue, opts);
+    const int64_t vec = 16 / elem_bytes(dtype);
+    const int64_t Kp = (K + vec - 1) / vec * vec;   // rows are repacked to a 16-byte multiple
+    const int id = grouped_config(G, total_m, N, Kp, dtype, epilogue, opts);
     return id >= 0 ? id : GEMM_MKL_STATUS_NOT_AVAILABLE;
 }
 
