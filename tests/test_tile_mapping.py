@@ -62,7 +62,7 @@ import tiled_dense_gemm_mkl_amd as gm  # noqa: E402
 
 
 @pytest.mark.parametrize("M,N,K,L,dtype,split", [
-    (512, 5632, 2048, 1, "bf16", None),      # 176 tiles, one round
+    (512, 5632, 2048, 1, "bf16", None),      # 236 tiles of 128 x 96, one round
     (8192, 8192, 8192, 1, "f16", None),      # blocked
     (4096, 8192, 2048, 1, "bf16", None),     # blocked
     (4096, 5632, 2048, 1, "bf16", None),
@@ -102,9 +102,10 @@ def test_library_map_refuses_short_output_and_other_grids():
         gm.tile_order(8192, 8192, 64, 1, code, gm.EPI_RELU, gm.make_opts(force_general=True))
     lib = gm.load()
     import numpy as np
-    out = np.zeros(4 * 175, np.int32)
+    grid = gm.get_plan(512, 5632, 2048, 1, code, gm.EPI_RELU)["grid"]
+    out = np.zeros(4 * (grid - 1), np.int32)
     assert lib.gemm_mkl_tile_order(512, 5632, 2048, 1, code, gm.EPI_RELU, None, out.ctypes.data, out.size) == -1
-    assert lib.gemm_mkl_tile_order(512, 5632, 2048, 1, code, gm.EPI_RELU, None, None, 4 * 176) == -1
-    out = np.zeros(4 * 176, np.int32)
+    assert lib.gemm_mkl_tile_order(512, 5632, 2048, 1, code, gm.EPI_RELU, None, None, 4 * grid) == -1
+    out = np.zeros(4 * grid, np.int32)
     assert lib.gemm_mkl_tile_order(512, 5632, 2048, 1, code, gm.EPI_RELU, None, out.ctypes.data, out.size) == 0
     assert lib.gemm_mkl_tile_order(0, 5632, 2048, 1, code, gm.EPI_RELU, None, None, 0) == 0

@@ -152,13 +152,26 @@ int check_args(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, int epilog
     return GEMM_MKL_STATUS_OK;
 }
 
-// Modelled time of one configuration, in cycles of one CU, for the heuristic.
-double model_cycles(const ConfigEntry &c, int dtype, int64_t M, int64_t N, int64_t K, int64_t L, int S)
+// Modelled time of one configuration at prefetch depth p, in cycles of one
+// CU, for the heuristic (p < 0: no workgroups sharing a CU).
+double model_cycles(const ConfigEntry &c, int dtype, int64_t M, int64_t N, int64_t K, int64_t L, int S, int p)
 {
     const int total_chunks = (int)((K * elem_bytes(dtype) + c.rb - 1) / c.rb);
     const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn) * L;
     const int64_t units = tiles * S;
-    const int64_t rounds = (units + kNumCUs - 1) / kNumCUs;
+    // Two workgroups share a CU when two prefetch rings fit in its 160 KB of
+    // LDS.  A round of w co-resident workgroups is taken to last 0.8 w times
+    // one workgroup's time (one alone leaves memory latency exposed that the
+    // other fills).  The factor was fitted on 48 bf16 shapes (M 256..4096,
+    // N 1024..8192, K 512..8192, two boxes), where it chose 64 x 64 tiles for
+    // 257..512 tiles of short K (e.g. 256 x 5632 x 512: 5.6 against 6.7 us on
+    // 128 x 128 tiles).  It is applied to 16-bit types only: on fp32 it would
+    // pick 8 splits for 128 x 2048 x 2048, measured slower than 4.
+    int64_t w = 1;
+    if (p >= 0 && dtype != GEMM_MKL_F32 && 2 * (int64_t)(c.bm + c.bn) * c.rb * (p + 1) <= 160 * 1024)
+        w = std::min<int64_t>(2, (units + kNumCUs - 1) / kNumCUs);
+    const int64_t rounds = (units + kNumCUs * w - 1) / (kNumCUs * w);
+    const double share = w > 1 ? 0.8 * (double)w : 1.0;
     const int chunks = (total_chunks + S - 1) / S;
     const double bk = (double)c.rb / elem_bytes(dtype);
     const double peak = dtype == GEMM_MKL_F32 ? 256.0 : 4096.0;  // flop / clk / CU
@@ -171,7 +184,7 @@ double model_cycles(const ConfigEntry &c, int dtype, int64_t M, int64_t N, int64
     const double operand_bytes = (double)L * (double)(M + N) * (double)K * elem_bytes(dtype);
     if (c.default_p <= 1 && operand_bytes > 2.0 * kMallBytes) eff *= 0.9;
     const double per_chunk = 2.0 * c.bm * c.bn * bk / (peak * eff) + 60.0;
-    double cyc = (double)rounds * (chunks * per_chunk + 1500.0);
+    double cyc = (double)rounds * (chunks * per_chunk * share + 1500.0);
     if (S > 1) {
         const double out = (double)L * M * N;
         const double bytes = out * 4.0 * S * 2.0 + out * elem_bytes(dtype);
@@ -219,7 +232,7 @@ double model_streamk_cycles(const ConfigEntry &c, int dtype, int64_t M, int64_t 
     const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn) * L;
     const int64_t U = tiles * C;
     const int64_t G = streamk_grid(U, C);
-    const double one_round = model_cycles(c, dtype, M, N, K, L, 1);
+    const double one_round = model_cycles(c, dtype, M, N, K, L, 1, -1);
     const int64_t rounds = (tiles + kNumCUs - 1) / kNumCUs;
     const double per_chunk = (one_round / (double)rounds - 1500.0) / (double)C;
     const int64_t per_wg = (U + G - 1) / G;
@@ -365,7 +378,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
             if (forced_s <= 0 && S > 1 && (total_chunks + S - 1) / S < 4) break;
             if (forced_s <= 0 && S != 1 && S != 2 && S != 3 && S != 4 && S != 6 && S != 8 && S != 12 && S != 16)
                 continue;
-            const double cyc = model_cycles(c, dtype, M, N, K, L, S);
+            const double cyc = model_cycles(c, dtype, M, N, K, L, S, p);
             if (cyc < best) {
                 best = cyc;
                 best_c = id;
@@ -695,7 +708,7 @@ int grouped_config(int64_t G, int64_t total_m, int64_t N, int64_t K, int dtype, 
         // tile sizes (groups of a few hundred rows run faster on 128-row than
         // on 256-row tiles).  A single group is a plain GEMM.
         const int64_t m_eff = G > 1 ? total_m + G * c.bm : total_m;
-        const double cyc = model_cycles(c, dtype, m_eff, N, K, 1, 1);
+        const double cyc = model_cycles(c, dtype, m_eff, N, K, 1, 1, -1);
         if (cyc < best_cyc) {
             best_cyc = cyc;
             best = id;

@@ -999,7 +999,7 @@ struct TileCore {
     template <int MODE, class OT>
     __device__ __forceinline__ void store_staged(OT *out, int64_t M, int64_t N)
     {
-        static_assert(THREADS % (BN * (int)sizeof(OT) / 16) == 0, "every thread stores whole rows of 16-byte columns");
+        static_assert(THREADS >= BN * (int)sizeof(OT) / 16, "one pass covers a whole row of 16-byte columns");
         lds_barrier();   // every wave's ring reads and loads are done
         stage_tile<MODE, OT>(smem);
         lds_barrier();   // the whole tile is in LDS
@@ -1008,6 +1008,18 @@ struct TileCore {
 
     // Bytes of one finished tile in the staged layout (output type T).
     static constexpr int STAGE_BYTES = BM * BN * (int)sizeof(T);
+
+    // Physical 16-byte column of logical column c in staged row r (NC columns
+    // per row): XOR with the row when NC is a power of two, else a rotation by
+    // the row (an XOR could leave the row, e.g. 11 ^ 4 = 15 with NC = 12).
+    template <int NC>
+    static __device__ __forceinline__ int stage_col(int c, int r)
+    {
+        if constexpr ((NC & (NC - 1)) == 0)
+            return c ^ (r & (NC - 1));
+        else
+            return (c + r) % NC;
+    }
 
     // The MFMA waves of k-group 0 write the finished tile (epilogue applied,
     // converted to OT) to `stage`, row-major with each row's 16-byte columns
@@ -1036,7 +1048,7 @@ struct TileCore {
                         y[q] = (MODE == MODE_PARTIAL) ? v : apply_epilogue<MODE>(v);
                     }
                     const int byte = cn * OES;
-                    char *dst = stage + r * ROWB + ((((byte >> 4) ^ (r % NC)) << 4) | (byte & 15));
+                    char *dst = stage + r * ROWB + ((stage_col<NC>(byte >> 4, r) << 4) | (byte & 15));
                     if constexpr (OES == 4)
                         *reinterpret_cast<f32x4v *>(dst) = f32x4v{y[0], y[1], y[2], y[3]};
                     else
@@ -1061,9 +1073,10 @@ struct TileCore {
         const int rpp = nthreads / NC;          // rows per pass
         const int c = t % NC;
         const bool vec16 = ((N * OES) & 15) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+        // (threads rpp * NC .. nthreads - 1 start at row BM and store nothing)
 #pragma unroll
-        for (int rr = t / NC; rr < BM; rr += rpp) {
-            const i32x4 v = *reinterpret_cast<const i32x4 *>(stage + rr * ROWB + ((c ^ (rr % NC)) << 4));
+        for (int rr = t < rpp * NC ? t / NC : BM; rr < BM; rr += rpp) {
+            const i32x4 v = *reinterpret_cast<const i32x4 *>(stage + rr * ROWB + (stage_col<NC>(c, rr) << 4));
             const int64_t gm = m0 + rr;
             const int64_t gn = n0 + c * EPC;
             if (gm >= M) continue;
