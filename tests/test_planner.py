@@ -1,0 +1,66 @@
+"""CPU tests of the planner's choices (no GPU involved): the measured plans of
+the named workloads, the two-workgroups-per-CU term of the 16-bit cost model,
+and the opt-in 128 x 96 tile."""
+import itertools
+
+import pytest
+
+import tiled_dense_gemm_mkl_amd as gm
+from tiled_dense_gemm_mkl_amd import workloads
+
+# plans measured best (or within timing noise) on MI355X for each workload
+NAMED = {
+    "bf16_512x5632x2048_relu": ("bf16 128x128 k64 waves2x2+4p mfma32", 4, 1),
+    "f16_8192x8192x8192_identity": ("f16 256x256 k64 waves2x4 mfma32", 1, 1),
+    "bf16_L8_512x3584x18944_silu": ("bf16 256x256 k32 waves2x2 mfma32", 4, 1),
+    "f32_128x2048x2048_relu": ("f32 64x64 k32 waves2x2 mfma16", 3, 4),
+    "f32_128x128x128_identity": ("f32 32x64 k32 waves1x2 mfma16", 2, 1),
+}
+
+
+def _plan(M, N, K, L, dtype, epi="relu", **kw):
+    return gm.get_plan(M, N, K, L, gm.DTYPE_CODES[dtype], gm.EPILOGUE_CODES[epi], gm.make_opts(**kw) if kw else None)
+
+
+@pytest.mark.parametrize("key", sorted(NAMED))
+def test_named_workloads_keep_their_measured_plans(key):
+    w = workloads.WORKLOADS[key]
+    p = _plan(w.M, w.N, w.K, w.L, w.dtype, w.epilogue)
+    assert (gm.config_names()[p["config_id"]], p["prefetch_stages"], p["split_k"]) == NAMED[key]
+
+
+def test_grouped_workload_keeps_its_configuration():
+    cid = gm.grouped_config(8, 4096, 5632, 2048, gm.BF16, gm.EPI_RELU)
+    assert gm.config_names()[cid] == "bf16 128x128 k64 waves2x2+4p mfma32"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("M,N", [(256, 5632), (256, 8192), (512, 3584)])
+def test_short_K_mid_grids_run_two_workgroups_per_CU(dtype, M, N):
+    """257..512 tiles of 64 x 64 with K = 512 (8 chunks): two depth-3 rings
+    (64 KB each) fit in a CU's LDS, so all tiles run at once; measured 5.5-5.8
+    against 6.7-6.9 us for 128 x 128 tiles."""
+    p = _plan(M, N, 512, 1, dtype)
+    tiles = -(-M // 64) * -(-N // 64)
+    assert 256 < tiles <= 512
+    assert gm.config_names()[p["config_id"]] == f"{dtype} 64x64 k64 waves2x2 mfma32"
+    assert (p["prefetch_stages"], p["split_k"]) == (3, 1)
+
+
+def test_fp32_model_has_no_occupancy_term():
+    """The same grid in fp32 keeps one workgroup per CU per round in the
+    model: it still splits the 128 x 2048 x 2048 shape 4 ways, not 8."""
+    p = _plan(128, 2048, 2048, 1, "f32")
+    assert p["split_k"] == 4
+
+
+def test_opt_in_tile_is_never_chosen_but_can_be_forced():
+    names = gm.config_names()
+    for dtype in ("bf16", "f16"):
+        for M, N, K in itertools.product((1, 256, 512, 1024, 4096), (96, 1024, 3584, 5632, 8192), (64, 512, 2048, 8192)):
+            p = _plan(M, N, K, 1, dtype)
+            assert "128x96" not in names[p["config_id"]], (dtype, M, N, K)
+        cid = names.index(f"{dtype} 128x96 k64 waves2x2+4p mfma16")
+        p = _plan(512, 5632, 2048, 1, dtype, config_id=cid)
+        assert p["config_id"] == cid and p["prefetch_stages"] == 4
+        assert p["grid"] == 4 * 59   # 5632 / 96 = 58.7 column tiles
