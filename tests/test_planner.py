@@ -47,11 +47,13 @@ def test_short_K_mid_grids_run_two_workgroups_per_CU(dtype, M, N):
     assert (p["prefetch_stages"], p["split_k"]) == (3, 1)
 
 
-def test_fp32_model_has_no_occupancy_term():
-    """The same grid in fp32 keeps one workgroup per CU per round in the
-    model: it still splits the 128 x 2048 x 2048 shape 4 ways, not 8."""
-    p = _plan(128, 2048, 2048, 1, "f32")
-    assert p["split_k"] == 4
+def test_fp32_two_workgroups_per_CU_only_where_measured_faster():
+    """fp32's weaker factor: 128 x 2048 x 2048 keeps 4 splits (256 units;
+    8 splits measured slower), while 1024 x 1024 x 4096 (256 tiles of 64 x 64)
+    splits in 2 so that two workgroups share each CU (72.7 against 78.4 us)."""
+    assert _plan(128, 2048, 2048, 1, "f32")["split_k"] == 4
+    p = _plan(1024, 1024, 4096, 1, "f32")
+    assert gm.config_names()[p["config_id"]] == "f32 64x64 k32 waves2x2 mfma16" and p["split_k"] == 2
 
 
 def test_opt_in_tile_is_never_chosen_but_can_be_forced():

@@ -160,18 +160,21 @@ double model_cycles(const ConfigEntry &c, int dtype, int64_t M, int64_t N, int64
     const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn) * L;
     const int64_t units = tiles * S;
     // Two workgroups share a CU when two prefetch rings fit in its 160 KB of
-    // LDS.  A round of w co-resident workgroups is taken to last 0.8 w times
+    // LDS.  A round of w co-resident workgroups is taken to last f w times
     // one workgroup's time (one alone leaves memory latency exposed that the
-    // other fills).  The factor was fitted on 48 bf16 shapes (M 256..4096,
-    // N 1024..8192, K 512..8192, two boxes), where it chose 64 x 64 tiles for
-    // 257..512 tiles of short K (e.g. 256 x 5632 x 512: 5.6 against 6.7 us on
-    // 128 x 128 tiles).  It is applied to 16-bit types only: on fp32 it would
-    // pick 8 splits for 128 x 2048 x 2048, measured slower than 4.
+    // other fills).  f = 0.8 for 16-bit types, fitted on 48 bf16 shapes
+    // (M 256..4096, N 1024..8192, K 512..8192, two boxes), where it chose
+    // 64 x 64 tiles for 257..512 tiles of short K (e.g. 256 x 5632 x 512: 5.6
+    // against 6.7 us on 128 x 128 tiles).  f = 0.95 for fp32, fitted on 36
+    // shapes (M 128..1024, N 1024..4096, K 512..4096), where it chose two
+    // workgroups per CU through a split for K = 4096 (1024 x 1024 x 4096: 72.7
+    // against 78.4 us); below 0.9 it would pick 8 splits for 128 x 2048 x 2048,
+    // measured slower than 4.
     int64_t w = 1;
-    if (p >= 0 && dtype != GEMM_MKL_F32 && 2 * (int64_t)(c.bm + c.bn) * c.rb * (p + 1) <= 160 * 1024)
+    if (p >= 0 && 2 * (int64_t)(c.bm + c.bn) * c.rb * (p + 1) <= 160 * 1024)
         w = std::min<int64_t>(2, (units + kNumCUs - 1) / kNumCUs);
     const int64_t rounds = (units + kNumCUs * w - 1) / (kNumCUs * w);
-    const double share = w > 1 ? 0.8 * (double)w : 1.0;
+    const double share = w > 1 ? (dtype == GEMM_MKL_F32 ? 0.95 : 0.8) * (double)w : 1.0;
     const int chunks = (total_chunks + S - 1) / S;
     const double bk = (double)c.rb / elem_bytes(dtype);
     const double peak = dtype == GEMM_MKL_F32 ? 256.0 : 4096.0;  // flop / clk / CU
