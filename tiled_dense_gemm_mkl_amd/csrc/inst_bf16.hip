@@ -13,7 +13,8 @@ void register_bf16(std::vector<ConfigEntry> &t, DtypeKernels &k)
         make_entry<T, 256, 256, 64, 2, 2, 32, 1, 2, 3, 4>(d, 4, 0.47f, "bf16 256x256 k32 waves2x2 mfma32")));
     t.push_back(make_entry<T, 256, 256, 64, 2, 4, 32, 2, 3, 4>(d, 3, 0.46f, "bf16 256x256 k32 waves2x4 mfma32"));
     t.push_back(make_entry<T, 256, 256, 64, 4, 2, 32, 2, 3, 4>(d, 3, 0.46f, "bf16 256x256 k32 waves4x2 mfma32"));
-    t.push_back(make_entry<T, 256, 256, 128, 2, 4, 32, 1>(d, 1, 0.48f, "bf16 256x256 k64 waves2x4 mfma32"));
+    t.push_back(with_grouped<T, 256, 256, 128, 2, 4, 0, 32, 1>(
+        make_entry<T, 256, 256, 128, 2, 4, 32, 1>(d, 1, 0.48f, "bf16 256x256 k64 waves2x4 mfma32")));
     t.push_back(make_entry<T, 256, 128, 128, 4, 2, 32, 1, 2>(d, 2, 0.42f, "bf16 256x128 k64 waves4x2 mfma32"));
     t.push_back(make_entry<T, 256, 256, 128, 2, 2, 32, 1>(d, 1, 0.4f, "bf16 256x256 k64 waves2x2 mfma32"));
     t.push_back(make_entry<T, 256, 128, 128, 2, 2, 32, 1, 2>(d, 2, 0.4f, "bf16 256x128 k64 waves2x2 mfma32"));
