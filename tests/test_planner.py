@@ -66,3 +66,13 @@ def test_opt_in_tile_is_never_chosen_but_can_be_forced():
         p = _plan(512, 5632, 2048, 1, dtype, config_id=cid)
         assert p["config_id"] == cid and p["prefetch_stages"] == 4
         assert p["grid"] == 4 * 59   # 5632 / 96 = 58.7 column tiles
+
+
+@pytest.mark.parametrize("G,rows,want", [
+    (8, 4096, "bf16 256x256 k64 waves2x4 mfma32"),    # 667 us against 826 on 128 x 128 + producers
+    (32, 2048, "bf16 256x256 k64 waves2x4 mfma32"),   # 1503 against 1795
+    (64, 64, "bf16 128x128 k64 waves2x2+4p mfma32"),  # 361 against 385 on 256 x 256
+])
+def test_grouped_tile_follows_group_size(G, rows, want):
+    cid = gm.grouped_config(G, G * rows, 5632, 2048, gm.BF16, gm.EPI_RELU)
+    assert gm.config_names()[cid] == want
