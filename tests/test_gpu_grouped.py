@@ -149,6 +149,34 @@ def test_grouped_workload_parity(orc):
         assert_bits_equal(Ci[r:r + 1], refi, f"integer row {r}")
 
 
+@pytest.mark.parametrize("dtype,epilogue", [("bf16", "silu"), ("f16", "relu")])
+def test_grouped_large_groups_parity(orc, dtype, epilogue):
+    """8 groups of 4096 rows (N = K = 2048): the automatic choice is the
+    256 x 256 tile with 2 x 4 waves at depth 1.  Checked against the oracle on
+    40 sampled rows, among them the first and last row of every group (every
+    column of each), and bit-exact on 16 of them with integer inputs."""
+    G, rows_per, N, K = 8, 4096, 2048, 2048
+    total_m = G * rows_per
+    cid = gm.grouped_config(G, total_m, N, K, gm.DTYPE_CODES[dtype], gm.EPILOGUE_CODES[epilogue])
+    assert gm.config_names()[cid] == f"{dtype} 256x256 k64 waves2x4 mfma32"
+    offs = np.arange(1, G + 1, dtype=np.int32) * rows_per
+    A, B = _operands(dtype, total_m, G, N, K, seed=77)
+    edges = np.concatenate([offs - rows_per, offs - 1])
+    rows = np.concatenate([edges, np.random.default_rng(1).choice(total_m, 40 - edges.size, replace=False)])
+    C = _run(A, B, offs, dtype, epilogue)
+    groups = np.searchsorted(offs, rows, side="right")
+    for r, g in zip(rows, groups):
+        ref = orc.gemm_grouped64(A[r:r + 1], B[g:g + 1], np.array([1], np.int32), dtype, epilogue)
+        err = tol_error(C[r:r + 1], ref, A, B, dtype, K)
+        assert err <= TOL[dtype], f"row {r} (group {g}): err {err:.3e}"
+    Ai, Bi = _operands(dtype, total_m, G, N, K, seed=78, integer=True)
+    Ci = _run(Ai, Bi, offs, dtype, "identity")
+    for r, g in zip(rows[:16], groups[:16]):
+        refi = orc.round_to_dtype(orc.gemm_grouped64(Ai[r:r + 1], Bi[g:g + 1], np.array([1], np.int32),
+                                                     dtype, "identity"), dtype)
+        assert_bits_equal(Ci[r:r + 1], refi, f"integer row {r}")
+
+
 def test_grouped_empty_problems_launch_nothing():
     for args in [(0, 8, 8, 64), (3, 0, 8, 64), (3, 8, 0, 64)]:
         G, total_m, N, K = args
