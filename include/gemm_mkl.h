@@ -101,7 +101,11 @@ int gemm_mkl(const void *A, const void *B, void *C,
  *
  * prefetch_stages: number of K chunks loaded ahead of the one being consumed
  *   (the global -> LDS prefetch ring holds prefetch_stages + 1 chunks); 0 is
- *   load-then-use with no prefetch, -1 is automatic.  Below -1 is
+ *   load-then-use with no prefetch, -1 is automatic.  This is the
+ *   prefetch_stages of the software-pipelined loop in section 3 of
+ *   "CUTLASS CuTe DSL 控制流编程指南": a prologue loads the first stages, then
+ *   iteration i loads stage i + prefetch_stages while it consumes stage i, and
+ *   a negative depth is an error there as it is here.  Below -1 is
  *   INVALID_VALUE (the depth must be 0 or greater); a depth that no kernel
  *   configuration provides is NOT_AVAILABLE.
  * split_k: number of K ranges computed by separate workgroups and summed in

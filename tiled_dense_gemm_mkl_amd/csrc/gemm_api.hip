@@ -15,6 +15,7 @@
 #include <algorithm>
 #include <cstring>
 #include <map>
+#include <memory>
 #include <mutex>
 #include <utility>
 #include <vector>
@@ -493,89 +494,106 @@ int cached_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gem
 // ---------------------------------------------------------------- internal workspace
 
 struct Workspace {
+    std::mutex mu;              // held while this entry grows (and while a call reads it)
     void *ptr = nullptr;        // split-K / stream-K partial sums
     size_t bytes = 0;
     void *counters = nullptr;   // stream-K per-tile counters: zero between calls
     size_t counter_bytes = 0;
 };
 
+// One entry per (device, stream).  g_ws_mutex guards only the map itself:
+// growing one stream's workspace synchronises that stream while holding that
+// entry's own mutex, so calls on other streams (other entries) never wait for
+// it.  Entries are never erased while the library is in use (only
+// gemm_mkl_release_workspace frees their buffers), so a reference taken under
+// g_ws_mutex stays valid after it is released.
 std::mutex g_ws_mutex;
-std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+std::map<std::pair<int, hipStream_t>, std::unique_ptr<Workspace>> g_ws;
 
-// Per-tile stream-K counters of (device, stream): zeroed when allocated, and
-// every completed stream-K call leaves them zero again.
-int get_counters(hipStream_t stream, size_t need, void **out)
+Workspace *ws_entry(hipStream_t stream, int *status)
 {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) {
         t_last_hip = e;
-        return GEMM_MKL_STATUS_HIP_ERROR;
+        *status = GEMM_MKL_STATUS_HIP_ERROR;
+        return nullptr;
     }
     std::lock_guard<std::mutex> g(g_ws_mutex);
-    Workspace &w = g_ws[std::make_pair(dev, stream)];
-    if (w.counter_bytes < need) {
-        if (w.counters) {
-            e = hipStreamSynchronize(stream);
-            if (e == hipSuccess) e = hipFree(w.counters);
-            w.counters = nullptr;
-            w.counter_bytes = 0;
-            if (e != hipSuccess) {
-                t_last_hip = e;
-                return GEMM_MKL_STATUS_HIP_ERROR;
-            }
-        }
-        size_t sz = need < (size_t)65536 ? (size_t)65536 : need;
-        e = hipMalloc(&w.counters, sz);
-        if (e != hipSuccess) {
-            (void)hipGetLastError();
-            w.counters = nullptr;
-            return GEMM_MKL_STATUS_WORKSPACE;
-        }
-        e = hipMemsetAsync(w.counters, 0, sz, stream);
+    std::unique_ptr<Workspace> &w = g_ws[std::make_pair(dev, stream)];
+    if (!w) w.reset(new Workspace);
+    *status = GEMM_MKL_STATUS_OK;
+    return w.get();
+}
+
+// Grows *ptr / *bytes to hold `need` bytes (at least `floor`); the caller
+// holds the entry's mutex.  The old buffer may still be read by work queued
+// on `stream`, so it is freed only after that stream has drained.
+int grow(hipStream_t stream, void **ptr, size_t *bytes, size_t need, size_t floor, bool zero)
+{
+    if (*bytes >= need) return GEMM_MKL_STATUS_OK;
+    hipError_t e;
+    if (*ptr) {
+        e = hipStreamSynchronize(stream);
+        if (e == hipSuccess) e = hipFree(*ptr);
+        *ptr = nullptr;
+        *bytes = 0;
         if (e != hipSuccess) {
             t_last_hip = e;
             return GEMM_MKL_STATUS_HIP_ERROR;
         }
-        w.counter_bytes = sz;
     }
-    *out = w.counters;
+    const size_t sz = need < floor ? floor : need;
+    e = hipMalloc(ptr, sz);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        *ptr = nullptr;
+        return GEMM_MKL_STATUS_WORKSPACE;
+    }
+    if (zero) {
+        e = hipMemsetAsync(*ptr, 0, sz, stream);
+        if (e != hipSuccess) {
+            t_last_hip = e;
+            return GEMM_MKL_STATUS_HIP_ERROR;
+        }
+    }
+    *bytes = sz;
     return GEMM_MKL_STATUS_OK;
 }
 
-int get_workspace(hipStream_t stream, size_t need, void **out)
+// The entry of (device, stream) locked into `lk` (kept locked until the
+// caller has enqueued the work that uses its buffers, so that a second thread
+// on the same stream cannot free them in between); `lk` may already hold it.
+Workspace *locked_entry(hipStream_t stream, std::unique_lock<std::mutex> &lk, int *status)
 {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) {
-        t_last_hip = e;
-        return GEMM_MKL_STATUS_HIP_ERROR;
-    }
+    Workspace *w = ws_entry(stream, status);
+    if (!w) return nullptr;
+    if (!lk.owns_lock()) lk = std::unique_lock<std::mutex>(w->mu);
+    return w;
+}
+
+// Per-tile stream-K counters of (device, stream): zeroed when allocated, and
+// every completed stream-K call leaves them zero again.
+int get_counters(hipStream_t stream, size_t need, void **out, std::unique_lock<std::mutex> &lk)
+{
+    int st;
+    Workspace *w = locked_entry(stream, lk, &st);
+    if (!w) return st;
+    st = grow(stream, &w->counters, &w->counter_bytes, need, (size_t)65536, true);
+    if (st != GEMM_MKL_STATUS_OK) return st;
+    *out = w->counters;
+    return GEMM_MKL_STATUS_OK;
+}
+
+int get_workspace(hipStream_t stream, size_t need, void **out, std::unique_lock<std::mutex> &lk)
+{
     if (env().has_ws_limit && need > env().ws_limit) return GEMM_MKL_STATUS_WORKSPACE;
-    std::lock_guard<std::mutex> g(g_ws_mutex);
-    Workspace &w = g_ws[std::make_pair(dev, stream)];
-    if (w.bytes < need) {
-        if (w.ptr) {
-            // the old buffer may still be read by work queued on this stream
-            e = hipStreamSynchronize(stream);
-            if (e == hipSuccess) e = hipFree(w.ptr);
-            w.ptr = nullptr;
-            w.bytes = 0;
-            if (e != hipSuccess) {
-                t_last_hip = e;
-                return GEMM_MKL_STATUS_HIP_ERROR;
-            }
-        }
-        size_t sz = need < ((size_t)1 << 20) ? ((size_t)1 << 20) : need;
-        e = hipMalloc(&w.ptr, sz);
-        if (e != hipSuccess) {
-            (void)hipGetLastError();
-            w.ptr = nullptr;
-            return GEMM_MKL_STATUS_WORKSPACE;
-        }
-        w.bytes = sz;
-    }
-    *out = w.ptr;
+    int st;
+    Workspace *w = locked_entry(stream, lk, &st);
+    if (!w) return st;
+    st = grow(stream, &w->ptr, &w->bytes, need, (size_t)1 << 20, false);
+    if (st != GEMM_MKL_STATUS_OK) return st;
+    *out = w->ptr;
     return GEMM_MKL_STATUS_OK;
 }
 
@@ -626,12 +644,13 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
         p.map = make_tile_map(plan.tiles_m, plan.tiles_n, (int)L, plan.S, plan.group_m, (int)plan.grid);
         // the workspace of split-K partials (from offset 0) and repacked operands
         void *ws = nullptr;
+        std::unique_lock<std::mutex> ws_lock;   // the internal workspace stays ours until launched
         if (!plan.streamk && plan.ws_bytes > 0) {
             if (o && o->workspace) {
                 if (o->workspace_bytes < plan.ws_bytes) return GEMM_MKL_STATUS_WORKSPACE;
                 ws = o->workspace;
             } else {
-                st = get_workspace(stream, plan.ws_bytes, &ws);
+                st = get_workspace(stream, plan.ws_bytes, &ws, ws_lock);
                 if (st != GEMM_MKL_STATUS_OK) return st;
             }
         }
@@ -660,9 +679,9 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
                 cnt = o->workspace;
                 ws = static_cast<char *>(o->workspace) + plan.sk_counter_bytes;
             } else {
-                st = get_workspace(stream, plan.ws_bytes - plan.sk_counter_bytes, &ws);
+                st = get_workspace(stream, plan.ws_bytes - plan.sk_counter_bytes, &ws, ws_lock);
                 if (st != GEMM_MKL_STATUS_OK) return st;
-                st = get_counters(stream, plan.sk_counter_bytes, &cnt);
+                st = get_counters(stream, plan.sk_counter_bytes, &cnt, ws_lock);
                 if (st != GEMM_MKL_STATUS_OK) return st;
             }
             StreamKParams sp;
@@ -780,6 +799,7 @@ int run_grouped(const void *A, const void *B, void *C, const int32_t *offs, int6
                      (long long)G, (long long)total_m, (long long)N, (long long)K, dtype, epilogue, c.name,
                      c.grouped_p, (long long)grid);
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+    std::unique_lock<std::mutex> ws_lock;   // the internal workspace stays ours until launched
     if (pack_a || pack_b) {
         const size_t bytes_a = pack_a ? ((size_t)(total_m * Kp * es) + 255) / 256 * 256 : 0;
         const size_t need = bytes_a + (pack_b ? ((size_t)(G * N * Kp * es) + 255) / 256 * 256 : 0);
@@ -788,7 +808,7 @@ int run_grouped(const void *A, const void *B, void *C, const int32_t *offs, int6
             if (o->workspace_bytes < need) return GEMM_MKL_STATUS_WORKSPACE;
             ws = o->workspace;
         } else {
-            const int st = get_workspace(stream, need, &ws);
+            const int st = get_workspace(stream, need, &ws, ws_lock);
             if (st != GEMM_MKL_STATUS_OK) return st;
         }
         char *w = static_cast<char *>(ws);
@@ -950,17 +970,21 @@ int gemm_mkl_release_workspace(void)
     int cur = 0;
     (void)hipGetDevice(&cur);
     for (auto &kv : g_ws) {
-        for (void *ptr : {kv.second.ptr, kv.second.counters}) {
-            if (!ptr) continue;
+        Workspace &w = *kv.second;
+        std::lock_guard<std::mutex> gw(w.mu);
+        for (void **ptr : {&w.ptr, &w.counters}) {
+            if (!*ptr) continue;
             hipError_t e = hipSetDevice(kv.first.first);
-            if (e == hipSuccess) e = hipFree(ptr);
+            if (e == hipSuccess) e = hipFree(*ptr);
             if (e != hipSuccess) {
                 t_last_hip = e;
                 st = GEMM_MKL_STATUS_HIP_ERROR;
             }
+            *ptr = nullptr;
         }
+        w.bytes = 0;
+        w.counter_bytes = 0;
     }
-    g_ws.clear();
     (void)hipSetDevice(cur);
     return st;
 }

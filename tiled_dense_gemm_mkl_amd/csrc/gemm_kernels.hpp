@@ -268,6 +268,11 @@ __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t num_record
 // are inline asm so that the compiler adds no conservative waits for them;
 // the ring waits on vmcnt explicitly.  A write of M0 needs one wait state
 // before an LDS-DMA instruction reads it, hence the s_nop.
+// Every one of these statements lists M0 as clobbered: the compiler then
+// never assigns one of their operands to M0 and never keeps a value of its
+// own in M0 across them.  The M0 that dma16_same_m0 reads is the one the last
+// dma16_set_m0 wrote; the compiled kernels contain no other write of M0
+// between the two (the ISA has no M0 write that is not one of ours).
 __device__ __forceinline__ void dma16_set_m0(i32x4 rsrc, uint32_t m0, uint32_t voffset, uint32_t soffset)
 {
     asm volatile("s_mov_b32 m0, %0\n\t"
@@ -275,7 +280,7 @@ __device__ __forceinline__ void dma16_set_m0(i32x4 rsrc, uint32_t m0, uint32_t v
                  "buffer_load_dwordx4 %1, %2, %3 offen lds"
                  :
                  : "s"(m0), "v"(voffset), "s"(rsrc), "s"(soffset)
-                 : "memory");
+                 : "memory", "m0");
 }
 
 // Load block j (1..3) of the four sharing the current M0.
@@ -284,15 +289,15 @@ __device__ __forceinline__ void dma16_same_m0(i32x4 rsrc, int j, uint32_t voffse
     switch (j) {
     case 1:
         asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:1024 lds" : : "v"(voffset), "s"(rsrc), "s"(soffset)
-                     : "memory");
+                     : "memory", "m0");
         break;
     case 2:
         asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:2048 lds" : : "v"(voffset), "s"(rsrc), "s"(soffset)
-                     : "memory");
+                     : "memory", "m0");
         break;
     default:
         asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:3072 lds" : : "v"(voffset), "s"(rsrc), "s"(soffset)
-                     : "memory");
+                     : "memory", "m0");
         break;
     }
 }
