@@ -184,6 +184,38 @@ int gemm_mkl_ex(const void *A, const void *B, void *C,
                 const gemm_mkl_opts *opts);
 
 /*
+ * gemm_mkl_ex for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  It
+ * computes what gemm_mkl_ex computes (same plans, same kernels, same bits
+ * for the same plan), but the split-K partial sums and repacked operands live
+ * in a fixed device scratch array of GEMM_MKL_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each device it runs on (allocated with the library's code
+ * when the library is first used on that device, and kept until the process
+ * ends).  The call allocates and frees nothing.
+ *
+ * opts: as for gemm_mkl_ex, except that opts->workspace must be NULL and
+ *   workspace_bytes 0 (INVALID_VALUE otherwise) and GEMM_MKL_OPT_STREAMK is
+ *   NOT_AVAILABLE (stream-K is never used here).  The automatic plan only
+ *   considers K splits whose partial sums fit the scratch; a plan that still
+ *   needs more than GEMM_MKL_NOALLOC_SCRATCH_BYTES (a forced split, or
+ *   repacked operands: K * element bytes not a multiple of 16, A or B not
+ *   16-byte aligned) returns GEMM_MKL_STATUS_WORKSPACE before anything is
+ *   launched, with C untouched.
+ *
+ * Every call on a device uses that device's one scratch array.  Calls that
+ * may overlap on one device (concurrent streams, or calls from several
+ * threads) race on it and are undefined; calls issued in order on one stream
+ * are safe.  No part of the scratch has to start at zero.  Ownership of A, B
+ * and C and the status codes are as for gemm_mkl_ex.
+ */
+#define GEMM_MKL_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+int gemm_mkl_noalloc(const void *A, const void *B, void *C,
+                     int64_t M, int64_t N, int64_t K, int64_t L,
+                     int dtype, int epilogue, void *stream,
+                     const gemm_mkl_opts *opts);
+
+/*
  * Grouped GEMM: G problems that share N and K but each have their own number
  * of rows, as the grouped matrix product reached through framework adapters on
  * "深入解析 CUTLASS CuTe DSL 的 JIT 函数参数生成机制" (section 5) does.  Group g

@@ -440,3 +440,27 @@ def test_planning_from_many_threads_matches_serial_planning():
                        cwd=root, timeout=120, check=True)
     serial = json.loads(r.stdout)
     assert [got[s] for s in shapes] == serial
+
+
+def test_noalloc_argument_checks(lib):
+    """gemm_mkl_noalloc's checks run before any HIP call: these calls never
+    reach the scratch or a kernel."""
+    call = lambda M, N, K, L, dtype, epi, o: lib.gemm_mkl_noalloc(  # noqa: E731
+        FAKE, FAKE, FAKE, M, N, K, L, dtype, epi, None, ctypes.byref(o) if o is not None else None)
+    # a caller workspace makes no sense here
+    assert call(64, 64, 64, 1, BF16, ID, gm.make_opts(workspace_ptr=FAKE, workspace_bytes=1 << 20)) == -1
+    # the checks of gemm_mkl_ex, in its order
+    assert call(64, 64, 64, 1, 7, ID, None) == -2
+    assert call(64, 64, 64, 1, BF16, 9, None) == -3
+    assert call(-1, 64, 64, 1, BF16, ID, None) == -1
+    assert call(64, 64, 64, 1, BF16, ID, gm.make_opts(prefetch_stages=-2)) == -1
+    # stream-K is not offered (its counters would have to start at zero)
+    assert call(512, 640, 2048, 1, BF16, ID, gm.make_opts(streamk=True)) == -6
+    # empty problems launch nothing
+    assert call(0, 64, 64, 1, BF16, ID, None) == 0
+    # a forced split whose partial sums exceed the scratch
+    need = gm.get_plan(512, 4096, 2048, 1, BF16, ID, gm.make_opts(split_k=16))["workspace_bytes"]
+    assert need > gm.NOALLOC_SCRATCH_BYTES
+    assert call(512, 4096, 2048, 1, BF16, ID, gm.make_opts(split_k=16)) == -4
+    # repacked operands that exceed it (K = 2047 bf16: A and B copied, 2 * 4096 * 2048 * 2 B each)
+    assert call(4096, 4096, 2047, 2, BF16, ID, None) == -4

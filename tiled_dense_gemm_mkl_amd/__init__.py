@@ -26,6 +26,8 @@ from ._binding import (  # noqa: F401
     gemm_grouped,
     gemm_mkl,
     gemm_mkl_ex,
+    gemm_mkl_noalloc,
+    NOALLOC_SCRATCH_BYTES,
     gemm_mkl_grouped,
     gemm_mkl_rms_norm,
     get_plan,

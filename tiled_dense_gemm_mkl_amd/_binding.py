@@ -27,6 +27,7 @@ OPT_STREAMK = 2
 OPT_NO_STREAMK = 4
 OPT_PERSISTENT = 8
 OPT_NO_PERSISTENT = 16
+NOALLOC_SCRATCH_BYTES = 32 << 20   # GEMM_MKL_NOALLOC_SCRATCH_BYTES
 
 DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16}
 EPILOGUE_CODES = {"identity": EPI_IDENTITY, "relu": EPI_RELU, "silu": EPI_SILU}
@@ -76,6 +77,7 @@ class Plan(ctypes.Structure):
 EXPORTS = (
     "gemm_mkl",
     "gemm_mkl_ex",
+    "gemm_mkl_noalloc",
     "gemm_mkl_grouped",
     "gemm_mkl_grouped_config",
     "gemm_mkl_opts_init",
@@ -112,6 +114,8 @@ def load(path: str = LIB_PATH):
     lib.gemm_mkl.restype = i32
     lib.gemm_mkl_ex.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i32, vp, ctypes.POINTER(Opts)]
     lib.gemm_mkl_ex.restype = i32
+    lib.gemm_mkl_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i32, vp, ctypes.POINTER(Opts)]
+    lib.gemm_mkl_noalloc.restype = i32
     lib.gemm_mkl_grouped.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, vp, ctypes.POINTER(Opts)]
     lib.gemm_mkl_grouped.restype = i32
     lib.gemm_mkl_grouped_config.argtypes = [i64, i64, i64, i64, i32, i32, ctypes.POINTER(Opts)]
@@ -189,6 +193,14 @@ def gemm_mkl(A_ptr, B_ptr, C_ptr, M, N, K, L, dtype, epilogue, stream=None) -> i
 def gemm_mkl_ex(A_ptr, B_ptr, C_ptr, M, N, K, L, dtype, epilogue, stream=None, opts: Opts | None = None) -> int:
     return load().gemm_mkl_ex(A_ptr, B_ptr, C_ptr, M, N, K, L, dtype, epilogue, stream,
                               ctypes.byref(opts) if opts is not None else None)
+
+
+def gemm_mkl_noalloc(A_ptr, B_ptr, C_ptr, M, N, K, L, dtype, epilogue, stream=None,
+                     opts: Opts | None = None) -> int:
+    """The allocation-free entry point (its workspace is the library's fixed
+    device scratch of NOALLOC_SCRATCH_BYTES); returns the status."""
+    return load().gemm_mkl_noalloc(A_ptr, B_ptr, C_ptr, M, N, K, L, dtype, epilogue, stream,
+                                   ctypes.byref(opts) if opts is not None else None)
 
 
 def gemm_mkl_grouped(A_ptr, B_ptr, C_ptr, offs_ptr, G, total_m, N, K, dtype, epilogue, stream=None,

@@ -25,6 +25,16 @@
 
 using namespace gmk;
 
+// ---------------------------------------------------------------- the allocation-free variant
+
+// Device scratch of gemm_mkl_noalloc: its split-K partial sums and repacked
+// operands live here instead of in memory the library allocates.  One copy
+// per device, allocated with the code object when the library is loaded on
+// that device and held until the process ends.  In host code `scratch` only
+// names the symbol; its device address comes from hipGetSymbolAddress.
+constexpr size_t kScratchBytes = GEMM_MKL_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
 namespace {
 
 constexpr int kNumCUs = 256;          // MI355X compute units (8 XCDs x 32)
@@ -245,8 +255,12 @@ double model_streamk_cycles(const ConfigEntry &c, int dtype, int64_t M, int64_t 
     return cyc;
 }
 
+// ws_cap > 0: the workspace the call can have (gemm_mkl_noalloc's scratch).
+// The automatic choice then skips splits whose partial sums would not fit;
+// a plan that still needs more (forced options, repacked operands) is
+// GEMM_MKL_STATUS_WORKSPACE.
 int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_mkl_opts *o, int align,
-              Plan *plan)
+              Plan *plan, size_t ws_cap = 0)
 {
     Registry &R = registry();
     const int64_t es = elem_bytes(dtype);
@@ -301,8 +315,12 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
             gemm_mkl_opts_init(&inner);
         inner.flags = (inner.flags & ~(GEMM_MKL_OPT_STREAMK | GEMM_MKL_OPT_PERSISTENT)) | GEMM_MKL_OPT_NO_STREAMK |
                       GEMM_MKL_OPT_NO_PERSISTENT;
+        const int64_t pack_bytes = (!rows_ok || !(align & kAlignA) ? (L * M * Kp * es + 255) / 256 * 256 : 0) +
+                                   (!rows_ok || !(align & kAlignB) ? (L * N * Kp * es + 255) / 256 * 256 : 0);
+        if (ws_cap > 0 && (size_t)pack_bytes + 256 > ws_cap) return GEMM_MKL_STATUS_WORKSPACE;
         Plan fast;
-        const int st = make_plan(M, N, Kp, L, dtype, &inner, kAlignAll, &fast);
+        const size_t inner_cap = ws_cap > 0 ? std::max<size_t>(ws_cap - (size_t)pack_bytes - 256, 1) : 0;
+        const int st = make_plan(M, N, Kp, L, dtype, &inner, kAlignAll, &fast, inner_cap);
         if (st != GEMM_MKL_STATUS_OK) return st;
         if (!fast.general) {
             *plan = fast;
@@ -320,6 +338,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
                 off += ((size_t)(L * N * Kp * es) + 255) / 256 * 256;
             }
             plan->ws_bytes = off;
+            if (ws_cap > 0 && off > ws_cap) return GEMM_MKL_STATUS_WORKSPACE;
             return GEMM_MKL_STATUS_OK;
         }
         // (a K too long for every tile configuration: the general kernel below)
@@ -382,6 +401,8 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
             if (forced_s <= 0 && S > 1 && (total_chunks + S - 1) / S < 4) break;
             if (forced_s <= 0 && S != 1 && S != 2 && S != 3 && S != 4 && S != 6 && S != 8 && S != 12 && S != 16)
                 continue;
+            if (ws_cap > 0 && S > 1 && forced_s <= 0 && (double)S * (double)(L * M * N) * 4.0 > (double)ws_cap)
+                continue;
             const double cyc = model_cycles(c, dtype, M, N, K, L, S, p);
             if (cyc < best) {
                 best = cyc;
@@ -440,6 +461,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
         plan->P = c.persist_p;
         plan->grid = std::min<int64_t>(tiles_all, kNumCUs);
     }
+    if (ws_cap > 0 && plan->ws_bytes > ws_cap) return GEMM_MKL_STATUS_WORKSPACE;
     return GEMM_MKL_STATUS_OK;
 }
 
@@ -447,20 +469,21 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
 // options, so each distinct request is planned once and then looked up.
 struct PlanKey {
     int64_t M, N, K, L;
+    int64_t ws_cap;
     int32_t dtype, aligned, config_id, prefetch, split, flags;
     bool operator<(const PlanKey &o) const
     {
         return std::memcmp(this, &o, sizeof(PlanKey)) < 0;
     }
 };
-static_assert(sizeof(PlanKey) == 56, "PlanKey must have no padding (compared bytewise)");
+static_assert(sizeof(PlanKey) == 64, "PlanKey must have no padding (compared bytewise)");
 
 std::mutex g_plan_mutex;
 std::map<PlanKey, std::pair<int, Plan>> g_plans;
 constexpr size_t kMaxCachedPlans = 4096;
 
 int cached_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_mkl_opts *o, int align,
-                Plan *plan)
+                Plan *plan, size_t ws_cap = 0)
 {
     PlanKey key;
     std::memset(&key, 0, sizeof key);
@@ -468,6 +491,7 @@ int cached_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gem
     key.N = N;
     key.K = K;
     key.L = L;
+    key.ws_cap = (int64_t)ws_cap;
     key.dtype = dtype;
     key.aligned = align;
     key.config_id = o ? o->config_id : -1;
@@ -483,7 +507,7 @@ int cached_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gem
         }
     }
     Plan fresh;
-    const int st = make_plan(M, N, K, L, dtype, o, align, &fresh);
+    const int st = make_plan(M, N, K, L, dtype, o, align, &fresh, ws_cap);
     std::lock_guard<std::mutex> g(g_plan_mutex);
     if (g_plans.size() >= kMaxCachedPlans) g_plans.clear();
     g_plans.emplace(key, std::make_pair(st, fresh));
@@ -597,8 +621,36 @@ int get_workspace(hipStream_t stream, size_t need, void **out, std::unique_lock<
     return GEMM_MKL_STATUS_OK;
 }
 
+std::mutex g_scratch_mutex;
+std::map<int, void *> g_scratch_ptr;   // device -> address of that device's `scratch`
+
+// The address of the current device's scratch, looked up once per device
+// (with that device current) and kept.
+int scratch_address(void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        t_last_hip = e;
+        return GEMM_MKL_STATUS_HIP_ERROR;
+    }
+    std::lock_guard<std::mutex> g(g_scratch_mutex);
+    auto it = g_scratch_ptr.find(dev);
+    if (it == g_scratch_ptr.end()) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr) {
+            t_last_hip = e != hipSuccess ? e : hipErrorInvalidSymbol;
+            return GEMM_MKL_STATUS_HIP_ERROR;
+        }
+        it = g_scratch_ptr.emplace(dev, ptr).first;
+    }
+    *out = it->second;
+    return GEMM_MKL_STATUS_OK;
+}
+
 int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int64_t L, int dtype, int epilogue,
-        void *stream_v, const gemm_mkl_opts *o)
+        void *stream_v, const gemm_mkl_opts *o, size_t ws_cap = 0)
 {
     int st = check_args(M, N, K, L, dtype, epilogue, o);
     if (st != GEMM_MKL_STATUS_OK) return st;
@@ -611,8 +663,14 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
     const int align = (al(A, 16) ? kAlignA : 0) | (al(B, 16) ? kAlignB : 0) | (al(C, 4 * es) ? kAlignC : 0);
 
     Plan plan;
-    st = cached_plan(M, N, K, L, dtype, o, align, &plan);
+    st = cached_plan(M, N, K, L, dtype, o, align, &plan, ws_cap);
     if (st != GEMM_MKL_STATUS_OK) return st;
+    // gemm_mkl_noalloc: every check is done; the scratch is the workspace
+    void *scratch_ws = nullptr;
+    if (ws_cap > 0) {
+        st = scratch_address(&scratch_ws);
+        if (st != GEMM_MKL_STATUS_OK) return st;
+    }
 
     Registry &R = registry();
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
@@ -649,6 +707,8 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
             if (o && o->workspace) {
                 if (o->workspace_bytes < plan.ws_bytes) return GEMM_MKL_STATUS_WORKSPACE;
                 ws = o->workspace;
+            } else if (scratch_ws) {
+                ws = scratch_ws;   // the plan fits it (ws_cap)
             } else {
                 st = get_workspace(stream, plan.ws_bytes, &ws, ws_lock);
                 if (st != GEMM_MKL_STATUS_OK) return st;
@@ -862,6 +922,25 @@ int gemm_mkl_ex(const void *A, const void *B, void *C, int64_t M, int64_t N, int
                 int epilogue, void *stream, const gemm_mkl_opts *opts)
 {
     return run(A, B, C, M, N, K, L, dtype, epilogue, stream, opts);
+}
+
+int gemm_mkl_noalloc(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int64_t L, int dtype,
+                     int epilogue, void *stream, const gemm_mkl_opts *opts)
+{
+    if (opts && (opts->workspace != nullptr || opts->workspace_bytes != 0)) return GEMM_MKL_STATUS_INVALID_VALUE;
+    gemm_mkl_opts o;
+    if (opts)
+        o = *opts;
+    else
+        gemm_mkl_opts_init(&o);
+    const int st = check_args(M, N, K, L, dtype, epilogue, &o);
+    if (st != GEMM_MKL_STATUS_OK) return st;
+    // stream-K needs counters that start at zero: not offered here
+    if (o.flags & GEMM_MKL_OPT_STREAMK) return GEMM_MKL_STATUS_NOT_AVAILABLE;
+    o.flags |= GEMM_MKL_OPT_NO_STREAMK;
+    // run() makes every check of gemm_mkl_ex, plans within the scratch and
+    // only then looks up the scratch: a rejected call touches no device state
+    return run(A, B, C, M, N, K, L, dtype, epilogue, stream, &o, kScratchBytes);
 }
 
 int gemm_mkl_grouped(const void *A, const void *B, void *C, const int32_t *offs, int64_t G, int64_t total_m,
