@@ -9,7 +9,7 @@ import pytest
 
 import tiled_dense_gemm_mkl_amd as gm
 from tiled_dense_gemm_mkl_amd import workloads
-from gpu_helpers import (TOL, assert_bits_equal, assert_close, require_gpu, run_gemm, sample_indices,
+from gpu_helpers import (TOL, assert_bits_equal, assert_close, require_gpu, run_gemm,
                          to_device, widen_bits)
 
 pytestmark = pytest.mark.gpu
@@ -110,7 +110,6 @@ def test_K_zero_gives_epilogue_of_zero(dtype, epi):
 # ---------------------------------------------------------------- the five workloads
 
 SMALL = ["f32_128x128x128_identity", "f32_128x2048x2048_relu"]
-LARGE = ["bf16_512x5632x2048_relu", "f16_8192x8192x8192_identity", "bf16_L8_512x3584x18944_silu"]
 
 
 @pytest.mark.parametrize("key", SMALL)
@@ -123,57 +122,17 @@ def test_workload_full_parity(orc, key):
     print(f"{key}: err {err:.3e} (tol {TOL[w.dtype]:.0e})")
 
 
-@pytest.mark.parametrize("key", LARGE)
-def test_workload_sampled_parity(orc, key):
-    """Full-size run in the benchmark's own launch configuration; sampled check."""
-    w = workloads.WORKLOADS[key]
-    A, B = workloads.make_inputs(w)
-    C = run_gemm(A, B, w.dtype, w.epilogue)
-    li, mi, ni = sample_indices(w.L, w.M, w.N, 3000, seed=w.seed)
-    ref = orc.gemm_entries64(A, B, w.dtype, w.epilogue, li, mi, ni)
-    got = C[li, mi, ni]
-    err = assert_close(got, ref, A, B, w.dtype, w.K, key)
-    assert np.all(np.isfinite(widen_bits(C, w.dtype)))
-    print(f"{key}: sampled err {err:.3e} (tol {TOL[w.dtype]:.0e})")
-
-
-@pytest.mark.parametrize("key", list(workloads.WORKLOADS))
+@pytest.mark.parametrize("key", SMALL)
 def test_workload_integer_inputs_bit_exact(orc, key):
     """Integer inputs in [-2, 2]: every fp32 partial sum is exact, so the GPU
-    must reproduce the oracle's single rounding bit for bit."""
+    must reproduce the oracle's single rounding bit for bit.  (The three large
+    workloads are checked in full in test_gpu_full_parity.py.)"""
     w = workloads.WORKLOADS[key]
     A, B = workloads.make_inputs(w, integer=True)
     epi = "relu" if w.epilogue == "silu" else w.epilogue
     C = run_gemm(A, B, w.dtype, epi)
-    if w.M * w.N * w.K * w.L <= 2 ** 31:
-        ref = orc.round_to_dtype(orc.gemm64(A, B, w.dtype, epi), w.dtype)
-        assert_bits_equal(C, ref, key)
-    else:
-        li, mi, ni = sample_indices(w.L, w.M, w.N, 4000, seed=w.seed + 1)
-        ref = orc.round_to_dtype(orc.gemm_entries64(A, B, w.dtype, epi, li, mi, ni), w.dtype)
-        assert_bits_equal(C[li, mi, ni], ref, key)
-
-
-def test_k_heavy_workload_through_split_k(orc):
-    """The K-heavy batched shape through the split-K path (forced S) and the
-    deterministic fixed-order reduction."""
-    import torch
-
-    w = workloads.WORKLOADS["bf16_L8_512x3584x18944_silu"]
-    A, B = workloads.make_inputs(w)
-    a, b = to_device(A, w.dtype), to_device(B, w.dtype)
-    li, mi, ni = sample_indices(w.L, w.M, w.N, 2000, seed=55)
-    ref = orc.gemm_entries64(A, B, w.dtype, w.epilogue, li, mi, ni)
-    for S in (2, 4):
-        plan = gm.get_plan(w.M, w.N, w.K, w.L, gm.BF16, gm.EPI_SILU, gm.make_opts(split_k=S))
-        assert plan["split_k"] == S and plan["workspace_bytes"] > 0
-        c1 = gm.gemm(a, b, w.epilogue, split_k=S)
-        c2 = gm.gemm(a, b, w.epilogue, split_k=S)
-        torch.cuda.synchronize()
-        C1 = workloads.torch_to_storage(c1)
-        assert_bits_equal(C1, workloads.torch_to_storage(c2), f"split {S} run-to-run")
-        err = assert_close(C1[li, mi, ni], ref, A, B, w.dtype, w.K, f"split {S}")
-        print(f"split-K S={S}: sampled err {err:.3e}")
+    ref = orc.round_to_dtype(orc.gemm64(A, B, w.dtype, epi), w.dtype)
+    assert_bits_equal(C, ref, key)
 
 
 # ---------------------------------------------------------------- invariants
@@ -192,7 +151,7 @@ def test_prefetch_depth_does_not_change_results(orc, dtype):
     for cid in _configs_of(dtype):
         outs = {}
         sk_outs = {}
-        for p in range(0, 5):
+        for p in range(0, 9):
             try:
                 sk = gm.get_plan(M, N, K, L, gm.DTYPE_CODES[dtype], gm.EPI_IDENTITY,
                                  gm.make_opts(config_id=cid, prefetch_stages=p, streamk=True))
