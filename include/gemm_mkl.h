@@ -130,16 +130,24 @@ int gemm_mkl(const void *A, const void *B, void *C,
  *   bitwise equal to it.  The automatic plan does not use it (it measured no
  *   faster than the data-parallel grid); GEMM_MKL_PERSISTENT=-1 lets the plan
  *   take it whenever there are more tiles than compute units, =1 always.
+ *   GEMM_MKL_OPT_FIXUP / GEMM_MKL_OPT_NO_FIXUP: a split plan sums its pieces
+ *   inside the GEMM kernel (split_k 2..6): the S pieces of a tile run on one
+ *   XCD, each stores its fp32 partial (it stays in that XCD's L2) and counts
+ *   itself in the tile's counter word with one atomic, and the last piece
+ *   adds the partials in ascending split order, applies the epilogue and
+ *   stores C.  No workgroup waits for another.  Results equal the split-K
+ *   grid with the separate reduction bit for bit.  GEMM_MKL_FIXUP=0/1/-1 in
+ *   the environment: never / always / by the model (the default, -1).
  * workspace / workspace_bytes: caller-owned device memory for split-K or
  *   stream-K partial sums and repacked operands (NULL = use the library's
  *   internal workspace).  It must hold the plan's workspace_bytes
  *   (gemm_mkl_get_plan, which assumes 16-byte aligned pointers: a misaligned
  *   A or B also needs its repacked copy, L * rows * Kp * element bytes
  *   rounded up to 256) and be 256-byte aligned; too small is
- *   GEMM_MKL_STATUS_WORKSPACE, before anything is launched.  A stream-K plan uses its
- *   first plan.counter_bytes bytes as per-tile counters: they must be zero
- *   before the first stream-K call with that workspace, and every completed
- *   call leaves them zero.
+ *   GEMM_MKL_STATUS_WORKSPACE, before anything is launched.  A stream-K or
+ *   fix-up plan uses its first plan.counter_bytes bytes as per-tile counters:
+ *   they must be zero before the first such call with that workspace, and
+ *   every completed call leaves them zero.
  *
  * The environment variables GEMM_MKL_FORCE_CONFIG, GEMM_MKL_STAGES and
  * GEMM_MKL_SPLIT_K supply the same three choices when opts leaves them
@@ -171,7 +179,16 @@ enum {
     GEMM_MKL_OPT_PERSISTENT = 8,    /* use the persistent grid (NOT_AVAILABLE unless the
                                        chosen configuration has one, with split_k 1 and
                                        its own prefetch depth) */
-    GEMM_MKL_OPT_NO_PERSISTENT = 16 /* never use the persistent grid */
+    GEMM_MKL_OPT_NO_PERSISTENT = 16, /* never use the persistent grid */
+    GEMM_MKL_OPT_FIXUP = 32,        /* split plans sum their pieces inside the GEMM kernel
+                                       (the in-kernel fix-up; NOT_AVAILABLE with a forced
+                                       split when the configuration has no fix-up kernel,
+                                       split_k > 6 or a depth other than its own) */
+    GEMM_MKL_OPT_NO_FIXUP = 64,     /* split plans use the separate reduction kernel */
+    GEMM_MKL_OPT_FIXUP_RECOMPUTE = 128 /* test hook: the piece that finishes a fix-up tile
+                                       computes every other piece's partial itself instead
+                                       of reading it (the path taken when a partial was
+                                       written on another XCD); same results */
 };
 
 /* Initialise opts to "all automatic". */
@@ -327,6 +344,9 @@ typedef struct gemm_mkl_plan {
     int32_t packed;           /* 1 if A and B are first copied into zero-padded,
                                  16-byte aligned rows in the workspace (K * elem
                                  not a multiple of 16 bytes) */
+    int32_t fixup;            /* 1 if the split_k pieces of each tile are summed inside
+                                 the GEMM kernel (no reduction launch); counter_bytes
+                                 then gives its per-tile counter words */
 } gemm_mkl_plan;
 
 int gemm_mkl_get_plan(int64_t M, int64_t N, int64_t K, int64_t L,
@@ -342,7 +362,9 @@ int gemm_mkl_get_plan(int64_t M, int64_t N, int64_t K, int64_t L,
  * caller; it must hold 4 * grid entries (gemm_mkl_get_plan gives the grid).
  * Argument checks as in gemm_mkl_get_plan; NOT_AVAILABLE when the plan uses
  * the general, stream-K or persistent kernel (no such per-workgroup tile),
- * INVALID_VALUE when out is NULL or too small.  Empty problems write
+ * INVALID_VALUE when out is NULL or too small.  For a fix-up plan the entries
+ * are (batch, piece, tile row, tile column), all -1 for a workgroup that
+ * holds no tile (past the last tile of its XCD's run).  Empty problems write
  * nothing.  Launches nothing.
  */
 int gemm_mkl_tile_order(int64_t M, int64_t N, int64_t K, int64_t L,

@@ -110,7 +110,7 @@ def test_workspace_flags_and_alignment(lib):
     with pytest.raises(gm.GemmMklError):
         gm.get_plan(64, 64, 64, 1, BF16, ID, o)
     o = gm.make_opts()
-    o.flags = 0x40  # unknown flag bit
+    o.flags = 0x100  # unknown flag bit
     with pytest.raises(gm.GemmMklError):
         gm.get_plan(64, 64, 64, 1, BF16, ID, o)
 
@@ -148,18 +148,24 @@ def test_plans_of_the_workloads(lib, key):
         need = -(-chunks // 7)
         assert p["split_k"] == 1 and p["grid"] == max(1, min(256, tiles * chunks // need))
         assert p["workspace_bytes"] == p["counter_bytes"] + 2 * p["grid"] * p["block_m"] * p["block_n"] * 4
+    elif p["fixup"]:
+        # split-K summed in the kernel: the pieces of a tile share an XCD
+        assert p["grid"] == -(-tiles // 8) * 8 * p["split_k"]
     else:
         assert p["grid"] == tiles * p["split_k"]
     if p["streamk"]:
         pass
+    elif p["fixup"]:
+        assert p["workspace_bytes"] == p["counter_bytes"] + tiles * p["split_k"] * p["block_m"] * p["block_n"] * 4
     elif p["split_k"] > 1:
         assert p["workspace_bytes"] == p["split_k"] * w.L * w.M * w.N * 4
     else:
         assert p["workspace_bytes"] == 0
-    # a forced split of the K-heavy shape goes through the split-K path
-    p2 = gm.get_plan(w.M, w.N, w.K, w.L, code, epi, gm.make_opts(split_k=2))
-    assert p2["split_k"] == 2 and p2["workspace_bytes"] == 2 * w.L * w.M * w.N * 4
-    assert gm.workspace_size(w.M, w.N, w.K, w.L, code, 2) == p2["workspace_bytes"]
+    # a forced split with the reduction kernel: [S][L][M][N] fp32 partials
+    p2 = gm.get_plan(w.M, w.N, w.K, w.L, code, epi, gm.make_opts(split_k=2, fixup=False))
+    assert p2["split_k"] == 2 and p2["fixup"] == 0 and p2["workspace_bytes"] == 2 * w.L * w.M * w.N * 4
+    p3 = gm.get_plan(w.M, w.N, w.K, w.L, code, epi, gm.make_opts(split_k=2))
+    assert gm.workspace_size(w.M, w.N, w.K, w.L, code, 2) == p3["workspace_bytes"]
 
 
 def _round256(n):
@@ -204,7 +210,7 @@ def test_every_prefetch_depth_of_a_config_is_plannable(lib):
     for cid, name in enumerate(names):
         dt = gm.DTYPE_CODES[name.split()[0]]
         ok = []
-        for p in range(0, 5):
+        for p in range(0, 9):
             try:
                 plan = gm.get_plan(300, 300, 1000, 1, dt, ID, gm.make_opts(config_id=cid, prefetch_stages=p))
                 assert plan["prefetch_stages"] == p and plan["config_id"] == cid
@@ -231,9 +237,9 @@ def test_streamk_plans(lib):
 
 def test_ctypes_struct_sizes_match_header(lib):
     # gemm_mkl_opts: 4 x int32, pointer, size_t
-    # gemm_mkl_plan: 4 x int32, int64, 4 x int32, size_t, 4 x int32
+    # gemm_mkl_plan: 4 x int32, int64, 4 x int32, size_t, 5 x int32 (+ 4 bytes of tail padding)
     assert ctypes.sizeof(gm._binding.Opts) == 32
-    assert ctypes.sizeof(gm._binding.Plan) == 64
+    assert ctypes.sizeof(gm._binding.Plan) == 72
 
 
 def test_streamk_only_where_instantiated(lib):
@@ -243,7 +249,7 @@ def test_streamk_only_where_instantiated(lib):
     have = set()
     for cid, name in enumerate(gm.config_names()):
         dt = gm.DTYPE_CODES[name.split()[0]]
-        for p in range(0, 5):
+        for p in range(0, 9):
             try:
                 plan = gm.get_plan(300, 200, 2112, 2, dt, ID, gm.make_opts(config_id=cid, prefetch_stages=p,
                                                                              streamk=True))

@@ -246,11 +246,14 @@ SHAPES = [  # (KSW, NMF, NRD, LOADS): k-steps per wave and chunk, MFMAs and read
     (4, 8, 6, 6),     # 128x256 k64, 4 waves of 64x128
     (2, 4, 4, 4),     # k-groups: 128x128 k64, 8 waves, 2 per k-group pair
     (8, 4, 4, 4),
+    (4, 6, 5, 10),    # 128x192 k64, 4 waves of 64x96 + 4 producers
+    (2, 4, 4, 4),     # 128x128 k32, 4 waves of 64x64 + 4 producers
+    (2, 6, 5, 5),     # 128x192 k32, 4 waves of 64x96 + 4 producers
 ]
 
 
 @pytest.mark.parametrize("shape", SHAPES)
-@pytest.mark.parametrize("P", [1, 2, 3, 4])
+@pytest.mark.parametrize("P", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("producers", [False, True])
 def test_ring_schedule_has_no_hazard(shape, P, producers):
     KSW, NMF, NRD, LOADS = shape

@@ -27,6 +27,9 @@ OPT_STREAMK = 2
 OPT_NO_STREAMK = 4
 OPT_PERSISTENT = 8
 OPT_NO_PERSISTENT = 16
+OPT_FIXUP = 32
+OPT_NO_FIXUP = 64
+OPT_FIXUP_RECOMPUTE = 128
 NOALLOC_SCRATCH_BYTES = 32 << 20   # GEMM_MKL_NOALLOC_SCRATCH_BYTES
 
 DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16}
@@ -68,6 +71,7 @@ class Plan(ctypes.Structure):
         ("counter_bytes", ctypes.c_int32),
         ("persistent", ctypes.c_int32),
         ("packed", ctypes.c_int32),
+        ("fixup", ctypes.c_int32),
     ]
 
     def as_dict(self) -> dict:
@@ -158,7 +162,8 @@ def status_string(status: int) -> str:
 
 
 def make_opts(prefetch_stages=None, split_k=None, config_id=None, force_general=False,
-              workspace_ptr=None, workspace_bytes=0, streamk=None, persistent=None) -> Opts:
+              workspace_ptr=None, workspace_bytes=0, streamk=None, persistent=None, fixup=None,
+              fixup_recompute=False) -> Opts:
     o = Opts()
     load().gemm_mkl_opts_init(ctypes.byref(o))
     if prefetch_stages is not None:
@@ -177,6 +182,12 @@ def make_opts(prefetch_stages=None, split_k=None, config_id=None, force_general=
         o.flags |= OPT_PERSISTENT
     elif persistent is False:
         o.flags |= OPT_NO_PERSISTENT
+    if fixup is True:
+        o.flags |= OPT_FIXUP
+    elif fixup is False:
+        o.flags |= OPT_NO_FIXUP
+    if fixup_recompute:
+        o.flags |= OPT_FIXUP_RECOMPUTE
     if workspace_ptr is not None:
         o.workspace = int(workspace_ptr)
         o.workspace_bytes = int(workspace_bytes)
@@ -288,7 +299,8 @@ def _torch_dtype_code(t) -> int:
 
 
 def gemm(a, b, epilogue: str = "identity", out=None, *, prefetch_stages=None, split_k=None,
-         config_id=None, force_general=False, workspace=None, stream=None, streamk=None, persistent=None):
+         config_id=None, force_general=False, workspace=None, stream=None, streamk=None, persistent=None,
+         fixup=None, fixup_recompute=False):
     """C = epilogue(a @ b^T) per batch, on the GPU through libgemm_mkl.
 
     a: [L, M, K] or [M, K]; b: [L, N, K] or [N, K] (same dtype, on one GPU,
@@ -329,7 +341,8 @@ def gemm(a, b, epilogue: str = "identity", out=None, *, prefetch_stages=None, sp
     ws_ptr = ws_bytes = None
     if workspace is not None:
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    opts = make_opts(prefetch_stages, split_k, config_id, force_general, ws_ptr, ws_bytes or 0, streamk, persistent)
+    opts = make_opts(prefetch_stages, split_k, config_id, force_general, ws_ptr, ws_bytes or 0, streamk, persistent,
+                     fixup, fixup_recompute)
     s = stream if stream is not None else torch.cuda.current_stream(a.device)
     with torch.cuda.device(a.device):
         st = gemm_mkl_ex(a3.data_ptr(), b3.data_ptr(), out3.data_ptr(), M, N, K, L,

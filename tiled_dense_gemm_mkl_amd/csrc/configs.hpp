@@ -11,12 +11,13 @@
 
 namespace gmk {
 
-constexpr int kMaxPrefetch = 4;   // prefetch_stages 0..4 (ring of 1..5 LDS slots)
+constexpr int kMaxPrefetch = 8;   // prefetch_stages 0..8 (ring of 1..9 LDS slots)
 constexpr int kModes = 4;         // identity, relu, silu, split-K partial
 
 typedef hipError_t (*TileLaunchFn)(const TileParams &p, int grid, hipStream_t stream);
 typedef hipError_t (*StreamKLaunchFn)(const StreamKParams &p, int grid, hipStream_t stream);
 typedef hipError_t (*GroupedLaunchFn)(const GroupedParams &p, int grid, hipStream_t stream);
+typedef hipError_t (*FixupLaunchFn)(const FixupParams &p, int grid, hipStream_t stream);
 typedef hipError_t (*ReduceLaunchFn)(const float *W, void *C, int64_t total, int split, hipStream_t stream);
 typedef hipError_t (*GeneralLaunchFn)(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
                                       int64_t L, hipStream_t stream);
@@ -40,6 +41,7 @@ struct ConfigEntry {
     int grouped_p;
     TileLaunchFn persist[3];                    // persistent grid by epilogue (depth persist_p), or null
     int persist_p;
+    FixupLaunchFn fixup[3];                     // split-K with the in-kernel fix-up (default_p), or null
 };
 
 struct DtypeKernels {
@@ -110,6 +112,26 @@ ConfigEntry with_persistent(ConfigEntry e)
     e.persist[MODE_RELU] = &launch_persistent<T, BM, BN, RB, WMW, WNW, MF, P, MODE_RELU, NP>;
     e.persist[MODE_SILU] = &launch_persistent<T, BM, BN, RB, WMW, WNW, MF, P, MODE_SILU, NP>;
     e.persist_p = P;
+    return e;
+}
+
+template <class T, int BM, int BN, int RB, int WMW, int WNW, int MF, int P, int MODE, int NP>
+hipError_t launch_fixup(const FixupParams &p, int grid, hipStream_t stream)
+{
+    hipLaunchKernelGGL((gemm_fixup_kernel<T, BM, BN, RB, WMW, WNW, MF, P, MODE, NP>), dim3(grid),
+                       dim3((WMW * WNW + NP) * 64), 0, stream, p);
+    return hipGetLastError();
+}
+
+// Adds the split-K kernels with the in-kernel fix-up (prefetch depth P, the
+// entry's default, NP producer waves) to an entry made by make_entry_kp with
+// the same tile and wave grid.
+template <class T, int BM, int BN, int RB, int WMW, int WNW, int NP, int MF, int P>
+ConfigEntry with_fixup(ConfigEntry e)
+{
+    e.fixup[MODE_IDENTITY] = &launch_fixup<T, BM, BN, RB, WMW, WNW, MF, P, MODE_IDENTITY, NP>;
+    e.fixup[MODE_RELU] = &launch_fixup<T, BM, BN, RB, WMW, WNW, MF, P, MODE_RELU, NP>;
+    e.fixup[MODE_SILU] = &launch_fixup<T, BM, BN, RB, WMW, WNW, MF, P, MODE_SILU, NP>;
     return e;
 }
 

@@ -33,6 +33,11 @@ using namespace gmk;
 // that device and held until the process ends.  In host code `scratch` only
 // names the symbol; its device address comes from hipGetSymbolAddress.
 constexpr size_t kScratchBytes = GEMM_MKL_NOALLOC_SCRATCH_BYTES;
+// Its last MiB holds the split-K fix-up's per-tile counter words: zero when
+// the library is loaded, nothing else writes there, and every completed call
+// leaves them zero.  Partial sums and repacked operands use the rest.
+constexpr size_t kScratchCounterBytes = (size_t)1 << 20;
+constexpr size_t kScratchDataBytes = kScratchBytes - kScratchCounterBytes;
 static __device__ __align__(256) char scratch[kScratchBytes];
 
 namespace {
@@ -41,6 +46,7 @@ constexpr int kNumCUs = 256;          // MI355X compute units (8 XCDs x 32)
 constexpr double kMallBytes = 256.0 * (1 << 20);   // memory-side (Infinity) cache
 constexpr int64_t kMaxSplit = 16;
 constexpr int64_t kMaxGroups = 65536;   // grouped GEMM: groups per call
+constexpr int64_t kMaxFixupTiles = 8192;   // fix-up counter lines (the no-alloc scratch keeps 1 MiB of them)
 
 struct Registry {
     std::vector<ConfigEntry> table;
@@ -73,14 +79,15 @@ int env_int(const char *name, int dflt)
 
 // The environment overrides, read once, at the first call that needs them.
 struct EnvSettings {
-    int force_config, stages, split_k, streamk, group_m, log, persistent;
+    int force_config, stages, split_k, streamk, group_m, log, persistent, fixup;
     bool has_ws_limit;
     size_t ws_limit;
     EnvSettings()
         : force_config(env_int("GEMM_MKL_FORCE_CONFIG", -1)), stages(env_int("GEMM_MKL_STAGES", -1)),
           split_k(env_int("GEMM_MKL_SPLIT_K", 0)), streamk(env_int("GEMM_MKL_STREAMK", 0)),
           group_m(env_int("GEMM_MKL_GROUP_M", 4)), log(env_int("GEMM_MKL_LOG", 0)),
-          persistent(env_int("GEMM_MKL_PERSISTENT", 0)), has_ws_limit(false), ws_limit(0)
+          persistent(env_int("GEMM_MKL_PERSISTENT", 0)), fixup(env_int("GEMM_MKL_FIXUP", -1)), has_ws_limit(false),
+          ws_limit(0)
     {
         const char *lim = std::getenv("GEMM_MKL_WORKSPACE_LIMIT");
         if (lim && *lim) {
@@ -111,6 +118,9 @@ struct Plan {
     bool general = false;
     bool streamk = false;
     bool persistent = false;       // persistent grid with one ring across each workgroup's tiles
+    bool fixup = false;            // split-K summed inside the GEMM kernel (no reduction launch)
+    int32_t fix_per = 0;           // fix-up: tiles per XCD
+    size_t fix_counter_bytes = 0;  // fix-up: per-tile counter words, 256-byte padded
     int64_t sk_units = 0;          // stream-K: tiles (all batches) * chunks per tile
     size_t sk_counter_bytes = 0;   // stream-K: per-tile counters, 256-byte padded
     int64_t grid = 0;
@@ -151,12 +161,14 @@ int check_args(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, int epilog
         if (o->split_k < 0) return GEMM_MKL_STATUS_INVALID_VALUE;
         if (o->config_id < -1) return GEMM_MKL_STATUS_INVALID_VALUE;
         const int32_t known = GEMM_MKL_OPT_FORCE_GENERAL | GEMM_MKL_OPT_STREAMK | GEMM_MKL_OPT_NO_STREAMK |
-                              GEMM_MKL_OPT_PERSISTENT | GEMM_MKL_OPT_NO_PERSISTENT;
+                              GEMM_MKL_OPT_PERSISTENT | GEMM_MKL_OPT_NO_PERSISTENT | GEMM_MKL_OPT_FIXUP |
+                              GEMM_MKL_OPT_NO_FIXUP | GEMM_MKL_OPT_FIXUP_RECOMPUTE;
         if (o->flags & ~known) return GEMM_MKL_STATUS_INVALID_VALUE;
         if ((o->flags & GEMM_MKL_OPT_STREAMK) && (o->flags & GEMM_MKL_OPT_NO_STREAMK))
             return GEMM_MKL_STATUS_INVALID_VALUE;
         if ((o->flags & GEMM_MKL_OPT_PERSISTENT) && (o->flags & GEMM_MKL_OPT_NO_PERSISTENT))
             return GEMM_MKL_STATUS_INVALID_VALUE;
+        if ((o->flags & GEMM_MKL_OPT_FIXUP) && (o->flags & GEMM_MKL_OPT_NO_FIXUP)) return GEMM_MKL_STATUS_INVALID_VALUE;
         if (o->workspace == nullptr && o->workspace_bytes != 0) return GEMM_MKL_STATUS_INVALID_VALUE;
         if (o->workspace && (reinterpret_cast<uintptr_t>(o->workspace) & 255)) return GEMM_MKL_STATUS_INVALID_VALUE;
     }
@@ -165,7 +177,8 @@ int check_args(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, int epilog
 
 // Modelled time of one configuration at prefetch depth p, in cycles of one
 // CU, for the heuristic (p < 0: no workgroups sharing a CU).
-double model_cycles(const ConfigEntry &c, int dtype, int64_t M, int64_t N, int64_t K, int64_t L, int S, int p)
+double model_cycles(const ConfigEntry &c, int dtype, int64_t M, int64_t N, int64_t K, int64_t L, int S, int p,
+                    bool fixup = false)
 {
     const int total_chunks = (int)((K * elem_bytes(dtype) + c.rb - 1) / c.rb);
     const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn) * L;
@@ -199,7 +212,13 @@ double model_cycles(const ConfigEntry &c, int dtype, int64_t M, int64_t N, int64
     if (c.default_p <= 1 && operand_bytes > 2.0 * kMallBytes) eff *= 0.9;
     const double per_chunk = 2.0 * c.bm * c.bn * bk / (peak * eff) + 60.0;
     double cyc = (double)rounds * (chunks * per_chunk * share + 1500.0);
-    if (S > 1) {
+    if (S > 1 && fixup) {
+        // every piece stores its fp32 partial tile, the last one reads the
+        // other S - 1 back through the L2 (about 45 B/clk per CU) after one
+        // device-scope atomic; in the model's units (about 1.8 x cycles)
+        const double tile_bytes = 4.0 * c.bm * c.bn;
+        cyc += (double)rounds * 1.8 * (tile_bytes * S / 45.0 + 1000.0);
+    } else if (S > 1) {
         const double out = (double)L * M * N;
         const double bytes = out * 4.0 * S * 2.0 + out * elem_bytes(dtype);
         cyc += bytes / 2000.0 + 5000.0;  // ~4.8 TB/s and one more launch
@@ -290,6 +309,15 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
         forced_s = 1;
         sk_mode = 0;
     }
+    // split-K summed inside the kernel: 0 never, 1 for every split plan, -1 by the model
+    int fix_mode = env().fixup;
+    if (o && (o->flags & GEMM_MKL_OPT_FIXUP)) fix_mode = 1;
+    if (o && (o->flags & GEMM_MKL_OPT_NO_FIXUP)) fix_mode = 0;
+    if (fix_mode == 1 && sk_mode == 1) {
+        if (o && (o->flags & GEMM_MKL_OPT_FIXUP) && (o->flags & GEMM_MKL_OPT_STREAMK))
+            return GEMM_MKL_STATUS_NOT_AVAILABLE;
+        fix_mode = 0;
+    }
 
     if (forced_cfg >= (int)R.table.size()) return GEMM_MKL_STATUS_NOT_AVAILABLE;
     if (forced_cfg >= 0 && R.table[forced_cfg].dtype != dtype) return GEMM_MKL_STATUS_NOT_AVAILABLE;
@@ -328,7 +356,9 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
             plan->Kp = Kp;
             plan->pack_a = !rows_ok || !(align & kAlignA);
             plan->pack_b = !rows_ok || !(align & kAlignB);
-            size_t off = (plan->ws_bytes + 255) / 256 * 256;
+            // repacked operands follow the partial sums (the data part; a
+            // fix-up plan's counters, when in the workspace, come first)
+            size_t off = (plan->ws_bytes - plan->fix_counter_bytes + 255) / 256 * 256;
             if (plan->pack_a) {
                 plan->off_a = off;
                 off += ((size_t)(L * M * Kp * es) + 255) / 256 * 256;
@@ -337,7 +367,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
                 plan->off_b = off;
                 off += ((size_t)(L * N * Kp * es) + 255) / 256 * 256;
             }
-            plan->ws_bytes = off;
+            plan->ws_bytes = plan->fix_counter_bytes + off;
             if (ws_cap > 0 && off > ws_cap) return GEMM_MKL_STATUS_WORKSPACE;
             return GEMM_MKL_STATUS_OK;
         }
@@ -372,7 +402,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
     // candidate (config, split) pairs and stream-K configurations
     double best = 1e300;
     int best_c = -1, best_s = 1;
-    bool best_sk = false;
+    bool best_sk = false, best_fix = false;
     for (int id = 0; id < (int)R.table.size(); ++id) {
         const ConfigEntry &c = R.table[id];
         if (c.dtype != dtype) continue;
@@ -403,12 +433,29 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
                 continue;
             if (ws_cap > 0 && S > 1 && forced_s <= 0 && (double)S * (double)(L * M * N) * 4.0 > (double)ws_cap)
                 continue;
-            const double cyc = model_cycles(c, dtype, M, N, K, L, S, p);
-            if (cyc < best) {
-                best = cyc;
-                best_c = id;
-                best_s = S;
-                best_sk = false;
+            if (S == 1 || fix_mode != 1) {
+                const double cyc = model_cycles(c, dtype, M, N, K, L, S, p);
+                if (cyc < best) {
+                    best = cyc;
+                    best_c = id;
+                    best_s = S;
+                    best_sk = false;
+                    best_fix = false;
+                }
+            }
+            const int64_t tiles_all = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn) * L;
+            const bool fix_ok = S > 1 && fix_mode != 0 && c.fixup[0] != nullptr && S <= kMaxFixupSplit &&
+                                p == c.default_p && tiles_all <= kMaxFixupTiles &&
+                                (ws_cap == 0 || (double)tiles_all * S * c.bm * c.bn * 4.0 <= (double)ws_cap);
+            if (fix_ok) {
+                const double cyc = model_cycles(c, dtype, M, N, K, L, S, p, true);
+                if (cyc < best) {
+                    best = cyc;
+                    best_c = id;
+                    best_s = S;
+                    best_sk = false;
+                    best_fix = true;
+                }
             }
         }
     }
@@ -437,6 +484,16 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
     plan->grid = (int64_t)plan->tiles_m * plan->tiles_n * plan->S * L;
     if (plan->grid > INT32_MAX) return GEMM_MKL_STATUS_NOT_AVAILABLE;
     plan->ws_bytes = plan->S > 1 ? (size_t)plan->S * (size_t)(L * M * N) * 4 : 0;
+    if (best_fix && plan->S > 1) {
+        // S pieces of every tile on one XCD: ceil(tiles / 8) tiles per XCD
+        const int64_t tiles_all = (int64_t)plan->tiles_m * plan->tiles_n * L;
+        plan->fixup = true;
+        plan->fix_per = (int32_t)((tiles_all + 7) / 8);
+        plan->grid = (int64_t)plan->fix_per * 8 * plan->S;
+        plan->fix_counter_bytes = ((size_t)tiles_all * kFixupCounterStride * 4 + 255) / 256 * 256;
+        // [counters][partial tiles: S per tile]
+        plan->ws_bytes = plan->fix_counter_bytes + (size_t)tiles_all * plan->S * c.bm * c.bn * 4;
+    }
     plan->streamk = best_sk;
     if (best_sk) {
         const int64_t tiles_all = (int64_t)plan->tiles_m * plan->tiles_n * L;
@@ -461,7 +518,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
         plan->P = c.persist_p;
         plan->grid = std::min<int64_t>(tiles_all, kNumCUs);
     }
-    if (ws_cap > 0 && plan->ws_bytes > ws_cap) return GEMM_MKL_STATUS_WORKSPACE;
+    if (ws_cap > 0 && plan->ws_bytes - plan->fix_counter_bytes > ws_cap) return GEMM_MKL_STATUS_WORKSPACE;
     return GEMM_MKL_STATUS_OK;
 }
 
@@ -678,7 +735,7 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
         std::fprintf(stderr, "gemm_mkl: M=%lld N=%lld K=%lld L=%lld dtype=%d epi=%d -> %s P=%d S=%d%s%s grid=%lld\n",
                      (long long)M, (long long)N, (long long)K, (long long)L, dtype, epilogue,
                      plan.general ? "general" : R.table[plan.config_id].name, plan.P, plan.S,
-                     plan.streamk ? " stream-K" : (plan.persistent ? " persistent" : ""),
+                     plan.streamk ? " stream-K" : (plan.persistent ? " persistent" : (plan.fixup ? " fix-up" : "")),
                      plan.packed ? " packed" : "", (long long)plan.grid);
 
     hipError_t e;
@@ -700,18 +757,26 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
         p.chunks_per_split = plan.chunks_per_split;
         p.total_chunks = plan.total_chunks;
         p.map = make_tile_map(plan.tiles_m, plan.tiles_n, (int)L, plan.S, plan.group_m, (int)plan.grid);
-        // the workspace of split-K partials (from offset 0) and repacked operands
-        void *ws = nullptr;
+        // the workspace of split-K partials (from offset 0) and repacked
+        // operands; a fix-up plan's counter words come first in a caller's
+        // workspace, and from a buffer of their own otherwise
+        void *ws = nullptr, *fix_cnt = nullptr;
         std::unique_lock<std::mutex> ws_lock;   // the internal workspace stays ours until launched
         if (!plan.streamk && plan.ws_bytes > 0) {
             if (o && o->workspace) {
                 if (o->workspace_bytes < plan.ws_bytes) return GEMM_MKL_STATUS_WORKSPACE;
-                ws = o->workspace;
+                fix_cnt = o->workspace;
+                ws = static_cast<char *>(o->workspace) + plan.fix_counter_bytes;
             } else if (scratch_ws) {
                 ws = scratch_ws;   // the plan fits it (ws_cap)
+                fix_cnt = static_cast<char *>(scratch_ws) + kScratchDataBytes;
             } else {
-                st = get_workspace(stream, plan.ws_bytes, &ws, ws_lock);
+                st = get_workspace(stream, plan.ws_bytes - plan.fix_counter_bytes, &ws, ws_lock);
                 if (st != GEMM_MKL_STATUS_OK) return st;
+                if (plan.fixup) {
+                    st = get_counters(stream, plan.fix_counter_bytes, &fix_cnt, ws_lock);
+                    if (st != GEMM_MKL_STATUS_OK) return st;
+                }
             }
         }
         if (plan.packed) {
@@ -753,6 +818,15 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
         } else if (plan.persistent) {
             p.C = C;
             e = c.persist[epilogue](p, (int)plan.grid, stream);
+        } else if (plan.fixup) {
+            p.C = C;
+            FixupParams fp;
+            fp.t = p;
+            fp.ws = reinterpret_cast<float *>(ws);
+            fp.counters = reinterpret_cast<uint32_t *>(fix_cnt);
+            fp.per = plan.fix_per;
+            fp.force_remote = (o && (o->flags & GEMM_MKL_OPT_FIXUP_RECOMPUTE)) ? 1 : 0;
+            e = c.fixup[epilogue](fp, (int)plan.grid, stream);
         } else if (plan.S == 1) {
             p.C = C;
             e = c.fn[plan.P][epilogue](p, (int)plan.grid, stream);
@@ -940,7 +1014,7 @@ int gemm_mkl_noalloc(const void *A, const void *B, void *C, int64_t M, int64_t N
     o.flags |= GEMM_MKL_OPT_NO_STREAMK;
     // run() makes every check of gemm_mkl_ex, plans within the scratch and
     // only then looks up the scratch: a rejected call touches no device state
-    return run(A, B, C, M, N, K, L, dtype, epilogue, stream, &o, kScratchBytes);
+    return run(A, B, C, M, N, K, L, dtype, epilogue, stream, &o, kScratchDataBytes);
 }
 
 int gemm_mkl_grouped(const void *A, const void *B, void *C, const int32_t *offs, int64_t G, int64_t total_m,
@@ -1003,7 +1077,8 @@ int gemm_mkl_get_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, int
     }
     out->workspace_bytes = plan.ws_bytes;
     out->streamk = plan.streamk ? 1 : 0;
-    out->counter_bytes = (int32_t)plan.sk_counter_bytes;
+    out->counter_bytes = (int32_t)(plan.streamk ? plan.sk_counter_bytes : plan.fix_counter_bytes);
+    out->fixup = plan.fixup ? 1 : 0;
     out->persistent = plan.persistent ? 1 : 0;
     out->packed = plan.packed ? 1 : 0;
     return GEMM_MKL_STATUS_OK;
@@ -1023,7 +1098,12 @@ int gemm_mkl_tile_order(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, i
     const TileMap m = make_tile_map(plan.tiles_m, plan.tiles_n, (int)L, plan.S, plan.group_m, (int)plan.grid);
     for (int64_t b = 0; b < plan.grid; ++b) {
         int l, s, tm, tn;
-        map_workgroup(m, (uint32_t)b, l, s, tm, tn);
+        if (plan.fixup) {
+            (void)fixup_map(m, plan.fix_per, (uint32_t)b, l, s, tm, tn);
+            if (l >= L) l = s = tm = tn = -1;   // past the last tile of its XCD's run
+        } else {
+            map_workgroup(m, (uint32_t)b, l, s, tm, tn);
+        }
         out[4 * b] = l;
         out[4 * b + 1] = s;
         out[4 * b + 2] = tm;

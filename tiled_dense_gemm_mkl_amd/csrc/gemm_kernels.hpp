@@ -333,13 +333,6 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p)
     return (uint32_t)reinterpret_cast<uintptr_t>(p);
 }
 
-// XOR swizzle of the 16-byte column of a 128-byte LDS row: keeps the 16 rows
-// read by one 16-lane MFMA operand group on distinct banks.
-__device__ __forceinline__ int swz(int row)
-{
-    return (row & 7) ^ ((row >> 3) & 1);
-}
-
 // Workgroup id -> logical tile id.  Hardware dispatches consecutive workgroup
 // ids round-robin over the 8 XCDs; this gives each XCD a contiguous range of
 // logical ids so that tiles sharing A rows or B columns share one L2.
@@ -366,16 +359,22 @@ __device__ __forceinline__ void raster(int tile, int tiles_m, int tiles_n, int g
 // ------------------------------------------------------------------ the tiled kernel
 
 // LDS row layout of one chunk: RB bytes per row (64 or 128), split in 16-byte
-// columns.  Column c of row r is stored at physical column c ^ swizzle(r):
-//   RB = 128 (8 columns): swizzle(r) = (r & 7) ^ ((r >> 3) & 1)
-//   RB =  64 (4 columns): swizzle(r) = (r >> 2) & 3
-// In both cases 16 consecutive rows read at one logical column land on 16
-// distinct 16-byte bank groups of a 256-byte bank row (and 8 consecutive rows
-// on 8 distinct groups of a 128-byte bank row).
-template <int RB>
+// columns.  Column c of row r is stored at physical column c ^ swizzle(r),
+// chosen for the read pattern of the MFMA shape MF (a 16-byte read per lane):
+//   RB = 128, MF = 32 (32 rows x 2 columns per read):
+//       swizzle(r) = (r & 7) ^ ((r >> 3) & 1)
+//   RB = 128, MF = 16 (16 rows x 4 columns per read): swizzle(r) = r & 7
+//   RB =  64, MF = 32 (32 rows x 2 columns per read): swizzle(r) = (r >> 2) & 3
+// Measured with a read-throughput probe (16 waves per CU): each form reads
+// at the rate of a linear 1 KB read (about 5 clocks per instruction per CU);
+// the MF = 32 form applied to the MF = 16 pattern takes 8 (a 2-way bank
+// conflict on every read), and no swizzle takes 16.
+template <int RB, int MF>
 __device__ __forceinline__ int row_swizzle(int r)
 {
-    if constexpr (RB == 128)
+    if constexpr (RB == 128 && MF == 16)
+        return r & 7;
+    else if constexpr (RB == 128)
         return (r & 7) ^ ((r >> 3) & 1);
     else
         return (r >> 2) & 3;
@@ -533,7 +532,7 @@ struct TileCore {
         // column ks * STEP_COLS + lane / MF
         lrow = lane % MF;
         lcol = lane / MF;
-        sw = row_swizzle<RB>(lrow);
+        sw = row_swizzle<RB, MF>(lrow);
         rd_a = (uint32_t)((wm * WTM + lrow) * RB);
         rd_b = (uint32_t)(BM * RB + (wn * WTN + lrow) * RB);
     }
@@ -566,7 +565,7 @@ struct TileCore {
         for (int j = 0; j < A_LOADS; ++j) {
             const int g = li * A_LOADS + j;
             const int r = g * ROWS_PER_LOAD + lane / NCH;
-            const int c = (lane % NCH) ^ row_swizzle<RB>(r);
+            const int c = (lane % NCH) ^ row_swizzle<RB, MF>(r);
             col_a[j] = c;
             voff_a[j] = (r < rows_a) ? (uint32_t)(r * k_bytes + c * 16 + kRsrcBias - (j & 3) * 1024) : kOutOfRange;
         }
@@ -574,7 +573,7 @@ struct TileCore {
         for (int j = 0; j < B_LOADS; ++j) {
             const int g = li * B_LOADS + j;
             const int r = g * ROWS_PER_LOAD + lane / NCH;
-            const int c = (lane % NCH) ^ row_swizzle<RB>(r);
+            const int c = (lane % NCH) ^ row_swizzle<RB, MF>(r);
             col_b[j] = c;
             voff_b[j] = (r < rows_b) ? (uint32_t)(r * k_bytes + c * 16 + kRsrcBias - (j & 3) * 1024) : kOutOfRange;
         }
@@ -1149,6 +1148,77 @@ struct TileCore {
         }
     }
 
+    // The accumulators of the MFMA waves as an fp32 tile in register order:
+    // group q of 4 floats of MFMA thread t at floats (q * NWM * 64 + t) * 4,
+    // so that every store and load is a coalesced 16-byte access.  Default
+    // cache policy: the stores complete in this XCD's L2, where a workgroup of
+    // the same XCD reads them back (split-K fix-up).
+    static constexpr int PARTIAL_FLOATS = NWM * 64 * NREG;
+
+    __device__ __forceinline__ void store_partial_l2(float *W)
+    {
+        static_assert(WK == 1, "one k-group holds the sums");
+        if (!mma) return;
+        const __amdgpu_buffer_rsrc_t r = partial_rsrc(W);
+#pragma unroll
+        for (int q = 0; q < NREG / 4; ++q)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, get4(q)), r,
+                                                   (q * NWM * 64 + (int)threadIdx.x) * 16, 0, 0);
+    }
+
+    // acc = sum over k = 0 .. S-1, in ascending k from the left, of the fp32
+    // tiles at W + k * PARTIAL_FLOATS (register order); tile `mine` (if
+    // 0 <= mine < S) is taken from the accumulators themselves, which hold
+    // exactly what was stored there.  MFMA waves only.
+    // the largest divisor of n that is at most 16 (register groups loaded per batch)
+    static constexpr int block_of(int n)
+    {
+        int b = n < 16 ? n : 16;
+        while (n % b) --b;
+        return b;
+    }
+
+    __device__ __forceinline__ void combine_l2(const float *W, int S, int mine)
+    {
+        if (!mma) return;
+        constexpr int NQ = NREG / 4;
+        constexpr int QB = block_of(NQ);
+        static_assert(NQ % QB == 0, "register blocks");
+        const __amdgpu_buffer_rsrc_t r = partial_rsrc(W);
+#pragma unroll
+        for (int q0 = 0; q0 < NQ; q0 += QB) {
+            f32x4v sum[QB];
+            for (int k = 0; k < S; ++k) {
+                f32x4v v[QB];
+                if (k == mine) {
+#pragma unroll
+                    for (int b = 0; b < QB; ++b) v[b] = get4(q0 + b);
+                } else {
+#pragma unroll
+                    for (int b = 0; b < QB; ++b)
+                        v[b] = __builtin_bit_cast(
+                            f32x4v, __builtin_amdgcn_raw_buffer_load_b128(
+                                        r, (k * PARTIAL_FLOATS + ((q0 + b) * NWM * 64 + (int)threadIdx.x) * 4) * 4,
+                                        0, 0));
+                }
+                if (k == 0) {
+#pragma unroll
+                    for (int b = 0; b < QB; ++b) sum[b] = v[b];
+                } else {
+#pragma unroll
+                    for (int b = 0; b < QB; ++b) {
+                        sum[b][0] += v[b][0];
+                        sum[b][1] += v[b][1];
+                        sum[b][2] += v[b][2];
+                        sum[b][3] += v[b][3];
+                    }
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < QB; ++b) set4(q0 + b, sum[b]);
+        }
+    }
+
     // A private fp32 copy of the accumulators (a stream-K partial tile), in
     // register order: group q of 4 floats of thread t at (q * THREADS + t) * 4,
     // so that every store and load is a coalesced 16-byte access.
@@ -1368,6 +1438,136 @@ __global__ __launch_bounds__((WAVES_M *WAVES_N + NP) * 64) void gemm_persistent_
     const int total = p.tiles_m * p.tiles_n * (int)p.L;
     const int ntiles = w < total ? (total - w + G - 1) / G : 0;
     c.template run_persistent<MODE>(p, w, G, ntiles, smem + Core::LDS_BYTES);
+}
+
+// ------------------------------------------------------------------ split-K with an in-kernel fix-up
+
+// The XCD (and so the L2) this wave runs on.
+__device__ __forceinline__ uint32_t xcc_id()
+{
+    uint32_t x;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(x));
+    return x & 15;
+}
+
+// Split-K (split_matmul_k of the compiler page's Tile-IR pass list) whose S
+// pieces of a tile are summed inside the GEMM kernel, with no second launch.
+//   - Placement: workgroup b runs on XCD b % 8 (the hardware hands workgroup
+//     ids to the XCDs round-robin).  Tile v of the [l][tile] order belongs to
+//     XCD x = v / per, and its piece s is workgroup ((v % per) * S + s) * 8 + x,
+//     so the S pieces of a tile share one XCD's L2, and each XCD's tiles are a
+//     contiguous run of the raster (they share operand rows and columns).
+//   - Each piece stores its fp32 partial tile (default cache policy: the
+//     stores complete in its XCD's L2), waits for them, then adds itself to
+//     the tile's counter word with one device-scope atomic: the arrival count
+//     in bits 0..7 and, for piece s, its XCD id + 1 in bits 8 + 4 s ..
+//     11 + 4 s.  The piece that brings the count to S is the last one: it
+//     resets the word to zero for the next call, adds the S partials in
+//     ascending s (its own from its registers), applies the epilogue once and
+//     stores C.  Nothing ever waits for another workgroup.
+//   - The last piece reads a partial through its own L2 only when the word
+//     says that piece ran on the same XCD.  Otherwise (not expected on this
+//     chip; forced by the host with force_remote, for tests) it recomputes
+//     that piece's partial itself over the same chunks in the same order,
+//     which gives the same bits.  Results are bitwise reproducible and equal
+//     to the split-K grid with the separate reduction (same partials, same
+//     order of additions).
+// Workgroup b of a fix-up grid -> tile v of the [l][tile] order (returned),
+// batch l, piece s, tile row and column.  Past the last tile of an XCD's run
+// it returns l = L (no tile): per * 8 >= tiles of all batches.
+__host__ __device__ __forceinline__ uint32_t fixup_map(const TileMap &m, int per, uint32_t b, int &l, int &s, int &tm,
+                                                       int &tn)
+{
+    const uint32_t rnd = b >> 3;
+    const uint32_t j = fdiv(rnd, m.d_split);
+    s = (int)(rnd - j * (uint32_t)m.split);
+    const uint32_t v = (b & 7) * (uint32_t)per + j;
+    const uint32_t lq = fdiv(v, m.d_tiles);
+    raster_map(m, v - lq * (uint32_t)m.tiles, tm, tn);
+    l = (int)lq;
+    return v;
+}
+
+struct FixupParams {
+    TileParams t;            // split = S (2..6), chunks_per_split, map (tiles, S, raster)
+    float *ws;               // [tiles of all batches][S] partial tiles
+    uint32_t *counters;      // one word per tile, kFixupCounterStride words apart, zero between calls
+    int32_t per;             // tiles per XCD: ceil(tiles of all batches / 8)
+    int32_t force_remote;    // treat every other piece as not visible (recompute)
+};
+
+constexpr int kMaxFixupSplit = 6;
+// Counter words 128 bytes apart, one per cache line: the atomics of different
+// tiles then never queue behind each other on one line.
+constexpr int kFixupCounterStride = 32;
+
+template <class T, int BM, int BN, int RB, int WAVES_M, int WAVES_N, int MF, int P, int MODE, int NP>
+__global__ __launch_bounds__((WAVES_M *WAVES_N + NP) * 64) void gemm_fixup_kernel(FixupParams fp)
+{
+    typedef TileCore<T, BM, BN, RB, WAVES_M, WAVES_N, MF, P, 1, NP> Core;
+    static_assert(Core::PARTIAL_FLOATS == BM * BN, "a partial tile holds the whole tile");
+    __shared__ __attribute__((aligned(1024))) char smem[Core::LDS_BYTES];
+    Core c;
+    c.init(smem);
+    const TileParams &p = fp.t;
+    asm volatile("" : : "s"(p.A), "s"(p.B), "s"(p.C), "s"(p.M), "s"(p.N), "s"(p.K), "s"(p.L),
+                 "s"(p.chunks_per_split), "s"(p.total_chunks), "s"(fp.ws), "s"(fp.counters));
+    const int S = p.split;
+    int l, s, tm, tn;
+    const uint32_t v = fixup_map(p.map, fp.per, blockIdx.x, l, s, tm, tn);
+    // (workgroups past the last tile of an XCD's run hold no tile)
+    if (l >= p.L || tm >= p.tiles_m || tn >= p.tiles_n) return;
+
+    const int cps = p.chunks_per_split;
+    const int chunk0 = s * cps;
+    const int nk = max(0, min(cps, p.total_chunks - chunk0));
+    c.setup(p, (int)l, tm, tn);
+    c.zero();
+    c.template run<true>(chunk0, nk);
+
+    float *slots = fp.ws + (int64_t)v * S * Core::PARTIAL_FLOATS;
+    c.store_partial_l2(slots + (int64_t)s * Core::PARTIAL_FLOATS);
+    wait_vmcnt<0>();   // this wave's partial stores have completed in the L2
+    __syncthreads();   // ... every wave's
+    uint32_t *flag = reinterpret_cast<uint32_t *>(smem);   // (the ring is no longer read)
+    if (threadIdx.x == 0) {
+        const uint32_t me = xcc_id();
+        const uint32_t add = 1u + ((me + 1u) << (8 + 4 * s));
+        uint32_t *cnt = fp.counters + (int64_t)v * kFixupCounterStride;
+        const uint32_t old = __hip_atomic_fetch_add(cnt, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t f = 0;
+        if ((int)(old & 0xffu) == S - 1) {   // the last piece of the tile
+            const uint32_t word = old + add;
+            uint32_t remote = 0;
+            for (int k = 0; k < S; ++k) {
+                const uint32_t xk = (word >> (8 + 4 * k)) & 15u;
+                if (k != s && (xk != me + 1u || fp.force_remote)) remote |= 1u << k;
+            }
+            __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            f = 1u | (remote << 1);
+        }
+        flag[0] = f;
+    }
+    __syncthreads();
+    const uint32_t f = flag[0];
+    if (!(f & 1u)) return;   // another piece finishes the tile
+    uint32_t remote = __builtin_amdgcn_readfirstlane(f >> 1);
+    const bool recomputed = remote != 0;
+    while (remote) {
+        // a piece whose partial this L2 cannot see: compute it here
+        const int k = __builtin_ctz(remote);
+        remote &= remote - 1;
+        const int ck = k * cps;
+        c.zero();
+        c.template run<false>(ck, max(0, min(cps, p.total_chunks - ck)));
+        c.store_partial_l2(slots + (int64_t)k * Core::PARTIAL_FLOATS);
+        wait_vmcnt<0>();
+        __syncthreads();
+    }
+    // (after a recomputation the registers hold another piece: every partial
+    // is read from its slot, this piece's own included)
+    c.combine_l2(slots, S, recomputed ? -1 : s);
+    c.template store<MODE>(reinterpret_cast<T *>(p.C) + (int64_t)l * p.M * p.N, p.M, p.N);
 }
 
 // ------------------------------------------------------------------ stream-K

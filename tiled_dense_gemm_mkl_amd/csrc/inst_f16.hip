@@ -9,8 +9,8 @@ void register_f16(std::vector<ConfigEntry> &t, DtypeKernels &k)
     typedef _Float16 T;
     const int d = GEMM_MKL_F16;
     //                  T  BM   BN   RB  waves MF  prefetch depths
-    t.push_back(with_grouped<T, 256, 256, 64, 2, 2, 0, 32, 4>(
-        make_entry<T, 256, 256, 64, 2, 2, 32, 1, 2, 3, 4>(d, 4, 0.47f, "f16 256x256 k32 waves2x2 mfma32")));
+    t.push_back(with_fixup<T, 256, 256, 64, 2, 2, 0, 32, 4>(with_grouped<T, 256, 256, 64, 2, 2, 0, 32, 4>(
+        make_entry<T, 256, 256, 64, 2, 2, 32, 1, 2, 3, 4>(d, 4, 0.47f, "f16 256x256 k32 waves2x2 mfma32"))));
     t.push_back(make_entry<T, 256, 256, 64, 2, 4, 32, 2, 3, 4>(d, 3, 0.46f, "f16 256x256 k32 waves2x4 mfma32"));
     t.push_back(make_entry<T, 256, 256, 64, 4, 2, 32, 2, 3, 4>(d, 3, 0.46f, "f16 256x256 k32 waves4x2 mfma32"));
     t.push_back(with_grouped<T, 256, 256, 128, 2, 4, 0, 32, 1>(
@@ -24,8 +24,9 @@ void register_f16(std::vector<ConfigEntry> &t, DtypeKernels &k)
         make_entry<T, 128, 128, 128, 2, 2, 32, 0, 1, 2, 3>(d, 3, 0.4f, "f16 128x128 k64 waves2x2 mfma32")));
     // producer waves: NP extra waves issue every global->LDS load
     //                     T  BM   BN   RB  waves WK NP MF  prefetch depths
-    t.push_back(with_persistent<T, 128, 128, 128, 2, 2, 4, 32, 3>(with_grouped<T, 128, 128, 128, 2, 2, 4, 32, 4>(
-        make_entry_kp<T, 128, 128, 128, 2, 2, 1, 4, 32, 2, 3, 4>(d, 4, 0.42f, "f16 128x128 k64 waves2x2+4p mfma32"))));
+    t.push_back(with_fixup<T, 128, 128, 128, 2, 2, 4, 32, 4>(with_persistent<T, 128, 128, 128, 2, 2, 4, 32, 3>(
+        with_grouped<T, 128, 128, 128, 2, 2, 4, 32, 4>(make_entry_kp<T, 128, 128, 128, 2, 2, 1, 4, 32, 2, 3, 4>(
+            d, 4, 0.42f, "f16 128x128 k64 waves2x2+4p mfma32")))));
     t.push_back(make_entry_kp<T, 128, 128, 128, 2, 2, 1, 2, 32, 2, 3>(d, 3, 0.41f, "f16 128x128 k64 waves2x2+2p mfma32"));
     // 96-column tiles, chosen only by configuration id (the bf16 table has the
     // measurements; f16 512 x 5632 x 2048: 17.6 vs 16.6 us on 128 x 128 + 4p)
@@ -46,6 +47,17 @@ void register_f16(std::vector<ConfigEntry> &t, DtypeKernels &k)
     t.push_back(make_entry<T, 128, 128, 128, 2, 2, 16, 2>(d, 2, 0.3f, "f16 128x128 k64 waves2x2 mfma16"));
     t.push_back(make_entry<T, 256, 256, 128, 2, 2, 16, 1>(d, 1, 0.4f, "f16 256x256 k64 waves2x2 mfma16"));
     t.push_back(make_entry<T, 256, 256, 128, 2, 4, 16, 1>(d, 1, 0.40f, "f16 256x256 k64 waves2x4 mfma16"));
+    // 128 x 192 tiles with four producer waves at depth 3 (four 40 KB slots:
+    // all of the LDS), for the K-split grids that put one workgroup on nearly
+    // every compute unit (512 x 5632: 120 tiles, two splits, 240 workgroups).
+    t.push_back(with_fixup<T, 128, 192, 128, 2, 2, 4, 32, 3>(
+        make_entry_kp<T, 128, 192, 128, 2, 2, 1, 4, 32, 3>(d, 3, 0.30f, "f16 128x192 k64 waves2x2+4p mfma32")));
+    // 32-wide K chunks with deep rings: a chunk is half the bytes of a 64-wide
+    // one, so the same 160 KB of LDS keeps more of them (and more bytes) in
+    // flight while the memory latency is covered
+    t.push_back(make_entry_kp<T, 128, 128, 64, 2, 2, 1, 4, 32, 4, 6, 8>(d, 6, 0.30f, "f16 128x128 k32 waves2x2+4p mfma32"));
+    t.push_back(with_fixup<T, 128, 192, 64, 2, 2, 4, 32, 6>(
+        make_entry_kp<T, 128, 192, 64, 2, 2, 1, 4, 32, 4, 6, 7>(d, 6, 0.30f, "f16 128x192 k32 waves2x2+4p mfma32")));
     fill_dtype_kernels<T>(k);
 }
 
