@@ -303,8 +303,12 @@ def test_grouped_option_checks(lib):
 
 def test_grouped_config_query(lib):
     names = gm.config_names()
-    # a few hundred rows per group: 128-row tiles; one huge group: 256-row tiles
+    # 4096 rows in 8 groups x 5632 x 2048: 256 x 256 tiles with 8 waves (the
+    # partly filled last tile of each group skips its empty row blocks)
     cid = gm.grouped_config(8, 4096, 5632, 2048, BF16, RELU)
+    assert names[cid] == "bf16 256x256 k64 waves2x4 mfma32"
+    # 16 groups of about 64 rows: 128-row tiles
+    cid = gm.grouped_config(16, 1024, 4096, 1024, BF16, RELU)
     assert names[cid].startswith("bf16 128x128")
     cid = gm.grouped_config(1, 8192, 8192, 8192, F16, ID)
     assert names[cid].startswith("f16 256x256")

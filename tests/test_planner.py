@@ -30,8 +30,11 @@ def test_named_workloads_keep_their_measured_plans(key):
 
 
 def test_grouped_workload_keeps_its_configuration():
+    """4096 rows in 8 groups x 5632 x 2048 bf16, measured with the empty row
+    blocks of each group's last tile skipped: 256 x 256 tiles with 8 waves
+    105 us, with 4 waves 115 us, 128 x 128 + 4 producers 132 us."""
     cid = gm.grouped_config(8, 4096, 5632, 2048, gm.BF16, gm.EPI_RELU)
-    assert gm.config_names()[cid] == "bf16 128x128 k64 waves2x2+4p mfma32"
+    assert gm.config_names()[cid] == "bf16 256x256 k64 waves2x4 mfma32"
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])

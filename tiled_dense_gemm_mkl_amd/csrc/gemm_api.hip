@@ -859,11 +859,14 @@ int grouped_config(int64_t G, int64_t total_m, int64_t N, int64_t K, int dtype, 
         if (forced >= 0 && id != forced) continue;
         if (o && o->prefetch_stages >= 0 && o->prefetch_stages != c.grouped_p) continue;
         if (!fast_path_ok(c, dtype, K)) continue;
-        // with several groups every group ends in a partly filled row tile;
-        // counting a whole tile per group matched the measured ranking of the
-        // tile sizes (groups of a few hundred rows run faster on 128-row than
-        // on 256-row tiles).  A single group is a plain GEMM.
-        const int64_t m_eff = G > 1 ? total_m + G * c.bm : total_m;
+        // with several groups every group ends in a partly filled row tile,
+        // about half a tile on average; the kernel skips the MFMAs of its
+        // empty row blocks, but the tile still takes a workgroup for one
+        // round.  Measured on 4096 rows in 8 groups x 5632 x 2048 bf16 (MFMAs
+        // skipped): 256 x 256 tiles with 8 waves 105 us, with 4 waves 115 us,
+        // 128 x 128 + 4 producers 132 us, 64 x 64 180 us; the model ranks them
+        // in that order.  A single group is a plain GEMM.
+        const int64_t m_eff = G > 1 ? total_m + G * c.bm / 2 : total_m;
         const double cyc = model_cycles(c, dtype, m_eff, N, K, 1, 1, -1);
         if (cyc < best_cyc) {
             best_cyc = cyc;

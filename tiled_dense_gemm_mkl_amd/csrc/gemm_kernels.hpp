@@ -440,7 +440,13 @@ template <class T> struct Mfma<T, 32> {
 //           that issues it for many cycles when the address unit is busy,
 //           which costs a computing wave its MFMA slots but costs a producer
 //           nothing.  Needs P >= 2.
-template <class T, int BM, int BN, int RB, int WAVES_M, int WAVES_N, int MF, int P, int WK = 1, int NP = 0>
+//   ILV     interleaved row blocks: fragment row i of wave row wm covers tile
+//           rows (i * WAVES_M + wm) * MF .. + MF - 1 (else wm * WTM + i * MF ..),
+//           so that the live rows of a partly filled tile are shared out
+//           evenly over the wave rows, and the MFMAs of whole MF-row blocks
+//           past the last row can be skipped (run_live).
+template <class T, int BM, int BN, int RB, int WAVES_M, int WAVES_N, int MF, int P, int WK = 1, int NP = 0,
+          bool ILV = false>
 struct TileCore {
     typedef Mfma<T, MF> MM;
     typedef typename MM::acc_t acc_t;
@@ -467,6 +473,7 @@ struct TileCore {
     static constexpr int A_LOADS = A_GROUPS / NL;
     static constexpr int B_LOADS = B_GROUPS / NL;
     static constexpr int LOADS = A_LOADS + B_LOADS;
+    static constexpr int FRAG_ROWS = ILV ? WAVES_M * MF : MF;   // tile rows between fragment rows i, i + 1
     static constexpr int NMF = FM * FN;                  // MFMAs per k-step
     static constexpr int NRD = FM + FN;                  // fragment reads per k-step
     static constexpr int NREG = FM * FN * MM::regs;      // accumulator floats per lane
@@ -533,8 +540,14 @@ struct TileCore {
         lrow = lane % MF;
         lcol = lane / MF;
         sw = row_swizzle<RB, MF>(lrow);
-        rd_a = (uint32_t)((wm * WTM + lrow) * RB);
+        rd_a = (uint32_t)((row_block(0) + lrow) * RB);
         rd_b = (uint32_t)(BM * RB + (wn * WTN + lrow) * RB);
+    }
+
+    // First tile row of fragment row i of this wave.
+    __device__ __forceinline__ int row_block(int i) const
+    {
+        return ILV ? (i * WAVES_M + wm) * MF : wm * WTM + i * MF;
     }
 
     // Buffer descriptors and per-lane offsets for tile (l, tm, tn).
@@ -661,7 +674,7 @@ struct TileCore {
         const char *base = smem + slot * SLOT_BYTES;
         const int col = (((kg * KSW + ks) * STEP_COLS + lcol) ^ sw) * 16;
         if (r < FM)
-            fa[buf][r] = *reinterpret_cast<const i32x4 *>(base + rd_a + r * MF * RB + col);
+            fa[buf][r] = *reinterpret_cast<const i32x4 *>(base + rd_a + r * FRAG_ROWS * RB + col);
         else
             fb[buf][r - FM] = *reinterpret_cast<const i32x4 *>(base + rd_b + (r - FM) * MF * RB + col);
     }
@@ -672,13 +685,28 @@ struct TileCore {
         acc[i][j] = MM::step(fb[buf][j], fa[buf][i], acc[i][j]);
     }
 
+    // Fragment read r of a k-step for a wave whose first FML fragment rows
+    // are live: r < FML reads A fragment r, the rest the FN B fragments (no
+    // reads at all when FML == 0).
+    template <int FML>
+    __device__ __forceinline__ void read_live(int slot, int ks, int buf, int r)
+    {
+        read_one(slot, ks, buf, r < FML ? r : FM + (r - FML));
+    }
+    template <int FML>
+    static constexpr int reads_live() { return FML > 0 ? FML + FN : 0; }
+
     // One k-step of chunk i (in `slot`): its MFMAs, interleaved with the
     // fragment reads of the k-step RA ahead (in `next` past the chunk's end)
     // and, in the first SPREAD k-steps, the loads of chunk `load_chunk` into
-    // slot `fill`.
+    // slot `fill`.  Only the MFMAs and reads of fragment rows 0 .. FML - 1;
+    // the loads are the same for every FML.
+    template <int FML = FM>
     __device__ __forceinline__ void step(int ks, int slot, int next, int fill, int load_chunk, bool valid)
     {
-        constexpr int LGAP = (NMF / LPK) > 0 ? (NMF / LPK) : 1;    // MFMAs between loads
+        constexpr int NMFL = FML * FN;
+        constexpr int NRDL = reads_live<FML>();
+        constexpr int LGAP = (NMFL / LPK) > 0 ? (NMFL / LPK) : 1;    // MFMAs between loads
         const int t = ks + RA;                 // k-step whose fragments are read now
         const bool in_next = t >= KSW;         // ... of the next chunk
         const int tks = in_next ? t - KSW : t;
@@ -686,9 +714,9 @@ struct TileCore {
         const int rslot = in_next ? next : slot;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int m = 0; m < NMF; ++m) {
+        for (int m = 0; m < NMFL; ++m) {
             mfma_one(ks % NB, m);
-            if (m < NRD) read_one(rslot, tks, tbuf, m);
+            if (m < NRDL) read_live<FML>(rslot, tks, tbuf, m);
             if (NP == 0 && ks < SPREAD && m % LGAP == 0 && m / LGAP < LPK) {
                 const int q = ks * LPK + m / LGAP;
                 if (q < LOADS) issue_one(load_chunk, fill, q, valid);
@@ -697,10 +725,10 @@ struct TileCore {
         }
         // reads and loads that did not fit between the MFMAs
 #pragma unroll
-        for (int r = NMF; r < NRD; ++r) read_one(rslot, tks, tbuf, r);
+        for (int r = NMFL; r < NRDL; ++r) read_live<FML>(rslot, tks, tbuf, r);
         if (NP == 0 && ks < SPREAD) {
 #pragma unroll
-            for (int u = (NMF + LGAP - 1) / LGAP; u < LPK; ++u) {
+            for (int u = (NMFL + LGAP - 1) / LGAP; u < LPK; ++u) {
                 const int q = ks * LPK + u;
                 if (q < LOADS) issue_one(load_chunk, fill, q, valid);
             }
@@ -819,9 +847,11 @@ struct TileCore {
     // load of this workgroup is in flight; on exit none is, and every wave is
     // past its last LDS read of the range.  FRESH: the workgroup's first use
     // of the slots (nothing can still be reading them).
-    template <bool FRESH = false>
+    template <bool FRESH = false, int FML = FM>
     __device__ void run(int c_begin, int nk)
     {
+        constexpr int NMFL = FML * FN;
+        constexpr int NRDL = reads_live<FML>();
         if constexpr (!FRESH) lds_barrier();   // the slots may still be read by a previous range
         if constexpr (P == 0) {
             for (int i = 0; i < nk; ++i) {
@@ -832,9 +862,9 @@ struct TileCore {
 #pragma unroll
                 for (int ks = 0; ks < KSW; ++ks) {
 #pragma unroll
-                    for (int r = 0; r < NRD; ++r) read_one(0, ks, ks & 1, r);
+                    for (int r = 0; r < NRDL; ++r) read_live<FML>(0, ks, ks & 1, r);
 #pragma unroll
-                    for (int t = 0; t < NMF; ++t) mfma_one(ks & 1, t);
+                    for (int t = 0; t < NMFL; ++t) mfma_one(ks & 1, t);
                 }
             }
         } else if constexpr (NP > 0) {
@@ -867,12 +897,12 @@ struct TileCore {
 #pragma unroll
                 for (int ks = 0; ks < RA; ++ks)
 #pragma unroll
-                    for (int r = 0; r < NRD; ++r) read_one(0, ks, ks % NB, r);
+                    for (int r = 0; r < NRDL; ++r) read_live<FML>(0, ks, ks % NB, r);
                 int slot = 0;
                 for (int i = 0; i < nk; ++i) {
                     const int next = (slot + 1 == SLOTS) ? 0 : slot + 1;
 #pragma unroll
-                    for (int ks = 0; ks < KSW; ++ks) step(ks, slot, next, 0, 0, false);
+                    for (int ks = 0; ks < KSW; ++ks) step<FML>(ks, slot, next, 0, 0, false);
                     block_barrier();
                     slot = next;
                 }
@@ -898,7 +928,7 @@ struct TileCore {
 #pragma unroll
             for (int ks = 0; ks < RA; ++ks)
 #pragma unroll
-                for (int r = 0; r < NRD; ++r) read_one(0, ks, ks % NB, r);
+                for (int r = 0; r < NRDL; ++r) read_live<FML>(0, ks, ks % NB, r);
             int slot = 0;
             int fill = P;   // slot that receives chunk i + P
             for (int i = 0; i < nk; ++i) {
@@ -915,7 +945,7 @@ struct TileCore {
                             lds_barrier();
                         }
                     }
-                    step(ks, slot, next, fill, load_chunk, valid);
+                    step<FML>(ks, slot, next, fill, load_chunk, valid);
                 }
                 if constexpr (P >= 2) {
                     wait_vmcnt<WAIT_CNT>();
@@ -927,6 +957,33 @@ struct TileCore {
             // the zero fills past the last chunk must land before the slots
             // are reused or the workgroup's LDS is released
             wait_vmcnt<0>();
+        }
+    }
+
+    // run() for a tile whose first `live` rows exist (live <= BM): each MFMA
+    // wave computes only its fragment rows that start above row `live`
+    // (interleaved rows: every wave row gets its share of the live blocks).
+    // The loads, waits and barriers are those of run() for every wave.
+    template <bool FRESH = false>
+    __device__ void run_live(int c_begin, int nk, int live)
+    {
+        static_assert(ILV, "row-block skipping shares the live blocks out over the wave rows");
+        const int blocks = (live + MF - 1) / MF;                 // live MF-row blocks
+        int fml = (blocks - wm + WAVES_M - 1) / WAVES_M;          // ... of this wave row
+        fml = fml < 0 ? 0 : (fml > FM ? FM : fml);
+        if (!mma) fml = FM;
+        run_fml<FRESH, FM>(c_begin, nk, fml);
+    }
+    template <bool FRESH, int F>
+    __device__ __forceinline__ void run_fml(int c_begin, int nk, int fml)
+    {
+        if constexpr (F <= 0) {
+            run<FRESH, 0>(c_begin, nk);
+        } else {
+            if (fml >= F)
+                run<FRESH, F>(c_begin, nk);
+            else
+                run_fml<FRESH, F - 1>(c_begin, nk, fml);
         }
     }
 
@@ -1039,7 +1096,7 @@ struct TileCore {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             if (kg != 0 || !mma) break;   // (k-group 0 holds the sums)
-            const int r = wm * WTM + i * MF + lrow;
+            const int r = row_block(i) + lrow;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
 #pragma unroll
@@ -1111,7 +1168,7 @@ struct TileCore {
         constexpr int GROUPS = MM::regs / 4;
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-            const int64_t m = m0 + wm * WTM + i * MF + lrow;
+            const int64_t m = m0 + row_block(i) + lrow;
             if (m >= M) continue;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
@@ -1341,8 +1398,10 @@ struct GroupedParams {
 // group, a wave prefix sum of the tile counts), so every wave of the
 // workgroup reaches the same answer.  Offsets are clamped to a non-decreasing
 // sequence in [0, total_m], so no offsets can address rows outside A or C.
+// With tr < 0 nothing is looked up: the scan runs over every group and
+// returns the total number of row tiles (g stays -1).
 template <int BM>
-__device__ __forceinline__ void find_group(const GroupedParams &gp, int tr, int &g, int &tm, int &row0, int &rows)
+__device__ __forceinline__ int find_group(const GroupedParams &gp, int tr, int &g, int &tm, int &row0, int &rows)
 {
     const int lane = threadIdx.x & 63;
     int before = 0;      // row tiles of the groups scanned so far
@@ -1371,31 +1430,51 @@ __device__ __forceinline__ void find_group(const GroupedParams &gp, int tr, int 
         }
         const int total = __shfl(incl, 63, 64);
         const int x = tr - before;
-        if (x < total) {
+        if (tr >= 0 && x < total) {
             const unsigned long long hit = __ballot(nt > 0 && x >= incl - nt && x < incl);
             const int src = __ffsll((long long)hit) - 1;
             g = j0 + src;
             tm = x - __shfl(incl - nt, src, 64);
             row0 = __shfl(start, src, 64);
             rows = __shfl(end - start, src, 64);
-            return;
+            return before + total;
         }
         before += total;
         prev_end = __shfl(end, 63, 64);
     }
+    return before;
 }
+
+// Up to this many groups every workgroup scans all of them first (at most 8
+// wave-wide steps), to spread exactly the tiles that exist over the XCDs.
+constexpr int kGroupedExactScan = 512;
 
 template <class T, int BM, int BN, int RB, int WAVES_M, int WAVES_N, int MF, int P, int MODE, int NP>
 __global__ __launch_bounds__((WAVES_M *WAVES_N + NP) * 64) void gemm_grouped_kernel(GroupedParams gp)
 {
-    typedef TileCore<T, BM, BN, RB, WAVES_M, WAVES_N, MF, P, 1, NP> Core;
+    typedef TileCore<T, BM, BN, RB, WAVES_M, WAVES_N, MF, P, 1, NP, true> Core;
     __shared__ __attribute__((aligned(1024))) char smem[Core::LDS_BYTES];
     // Group-major order: group g owns the R_g * tiles_n consecutive ids after
     // those of groups 0 .. g-1 (R_g = its row tiles), and inside a group the
     // tiles follow the usual raster.  Tiles that share a column block of B[g]
     // then run close together, on one XCD, and no raster group mixes two
     // groups' B.
-    const int t = xcd_remap(blockIdx.x, gridDim.x);
+    // The grid covers an upper bound of the tiles (the offsets live on the
+    // device).  With few groups the exact count T is scanned first and XCD x
+    // (workgroups b = x, x + 8, ...) takes the x-th of 8 contiguous runs of
+    // about T / 8 tiles, so that no XCD is left with the empty ids at the
+    // end; otherwise the ids are remapped over the whole grid.
+    int t;
+    if (gp.G <= kGroupedExactScan) {
+        int g0, t0, r0, n0;
+        const int total = find_group<BM>(gp, -1, g0, t0, r0, n0) * gp.tiles_n;
+        const int x = (int)(blockIdx.x & 7), j = (int)(blockIdx.x >> 3);
+        const int q = total >> 3, rem = total & 7;
+        if (j >= q + (x < rem ? 1 : 0)) return;   // (the same for every wave)
+        t = x * q + min(x, rem) + j;
+    } else {
+        t = xcd_remap(blockIdx.x, gridDim.x);
+    }
     const int v = t / gp.tiles_n;   // the v-th row tile of the concatenated groups
     int g, tv, row0, rows;
     find_group<BM>(gp, v, g, tv, row0, rows);
@@ -1416,7 +1495,8 @@ __global__ __launch_bounds__((WAVES_M *WAVES_N + NP) * 64) void gemm_grouped_ker
     p.L = 1;
     c.setup(p, 0, tm, (int)tn);
     c.zero();
-    c.template run<true>(0, gp.total_chunks);
+    // a group's last row tile computes only its row blocks that hold rows
+    c.template run_live<true>(0, gp.total_chunks, min(rows - tm * BM, BM));
     c.template store<MODE>(p.C, rows, gp.N);
 }
 
