@@ -36,6 +36,10 @@ CASES = [
     ("bf16", 270, 390, 1552, 2, 4, "bf16 128x128 k64 waves2x2+4p mfma32"),
     ("f16", 129, 257, 2048, 1, 6, "f16 128x128 k64 waves2x2+4p mfma32"),
     ("bf16", 300, 520, 4096, 1, 2, "bf16 256x256 k32 waves2x2 mfma32"),
+    ("bf16", 512, 5632, 2048, 1, 2, "bf16 128x256 k64 waves2x2+4p mfma32"),
+    ("f16", 300, 700, 1552, 2, 3, "f16 128x256 k64 waves2x2+4p mfma32"),
+    ("bf16", 520, 390, 2048, 1, 2, "bf16 256x128 k64 waves2x2+4p mfma32"),
+    ("bf16", 260, 600, 1040, 1, 4, "bf16 128x256 k32 waves2x2+4p mfma32"),
     ("f32", 128, 2048, 2048, 1, 4, "f32 64x64 k32 waves2x2 mfma16"),
     ("f32", 100, 300, 520, 3, 3, "f32 64x64 k32 waves2x2 mfma16"),
     ("f32", 200, 200, 1024, 1, 2, "f32 128x128 k32 waves2x2 mfma32"),

@@ -87,9 +87,10 @@ def schedule(KSW, NMF, NRD, LOADS, P, nk, producers=False, mut=None, tile_chunks
         ev.append(("wait", 0))
         return [ev], KSW * NMF, KSW * NRD
 
-    # producer waves load, MFMA waves read and compute.  The data-parallel
-    # producers load real chunks only and wait for exactly the loads that
-    # follow the chunk they need (wait_chunks_after); the persistent ring
+    if not tile_chunks:
+        return producer_ring(KSW, NMF, NRD, LOADS, P, nk, RA, NB, SLOTS, WIN, mut)
+
+    # producer waves load, MFMA waves read and compute.  The persistent ring
     # keeps one load count per unit with zero fills.
     def tail_wait(j):
         if mut == "steady_tail_wait":
@@ -141,6 +142,58 @@ def schedule(KSW, NMF, NRD, LOADS, P, nk, producers=False, mut=None, tile_chunks
             if mut != "no_stage_barrier":
                 mma.append(("bar", False))
             mma.append(("stage_r", k))
+        slot = nxt
+    return [prod, mma], KSW * NMF, KSW * NRD
+
+
+def producer_ring(KSW, NMF, NRD, LOADS, P, nk, RA, NB, SLOTS, WIN, mut):
+    """The data-parallel producer ring: the producers issue every slot's
+    chunk up front, and the MFMA waves meet them at k-step WIN of each chunk i
+    (the barrier drains the MFMA waves' LDS reads): slot i is then free and
+    chunk i + 1 has landed; right after it the producers issue chunk
+    i + SLOTS into slot i.  Only real chunks are loaded, and each wait allows
+    exactly the loads issued after the chunk it needs (wait_chunks_after)."""
+    def allowed(j, cap):
+        if mut == "steady_tail_wait":
+            return LOADS * cap
+        return LOADS * max(0, min(j, cap)) + (mut == "loose_wait")
+
+    prod, mma = [], []
+    for c in range(min(SLOTS, nk)):
+        for q in range(LOADS):
+            prod.append(("load", c, c))
+    prod.append(("wait", allowed(min(SLOTS, nk) - 1, P)))
+    prod.append(("bar", False))
+    fill = 0 if mut != "slot_off" else 1
+    for i in range(nk):
+        prod.append(("wait", allowed(min(i + P, nk - 1) - (i + 1), P - 1)))
+        if mut != "no_barrier":
+            prod.append(("bar", False))
+        if i + SLOTS < nk:
+            for q in range(LOADS):
+                prod.append(("load", i + SLOTS, fill))
+        fill = (fill + 1) % SLOTS
+    prod.append(("wait", 0))
+    mma.append(("bar", False))
+    for ks in range(RA):
+        for r in range(NRD):
+            mma.append(("read", 0, 0, ks, ks % NB))
+    slot = 0
+    for i in range(nk):
+        nxt = (slot + 1) % SLOTS
+        for ks in range(KSW):
+            if ks == WIN and mut != "no_barrier":
+                mma.append(("bar", mut != "no_drain"))
+            t = ks + RA
+            in_next = t >= KSW
+            tks = t - KSW if in_next else t
+            rs, rc = (nxt, i + 1) if in_next else (slot, i)
+            for m in range(NMF):
+                mma.append(("mfma", i, ks, ks % NB))
+                if m < NRD:
+                    mma.append(("read", rs, rc, tks, t % NB))
+            for r in range(NMF, NRD):
+                mma.append(("read", rs, rc, tks, t % NB))
         slot = nxt
     return [prod, mma], KSW * NMF, KSW * NRD
 
@@ -259,7 +312,7 @@ def test_ring_schedule_has_no_hazard(shape, P, producers):
     KSW, NMF, NRD, LOADS = shape
     if producers and P < 2:
         pytest.skip("producer waves need P >= 2")
-    if LOADS * P >= 64:
+    if LOADS * (P + (1 if producers else 0)) >= 64:
         pytest.skip("beyond the vmcnt range")
     for nk in (1, 2, 3, 4, 5, 7, 16):
         roles, mpc, rpc = schedule(KSW, NMF, NRD, LOADS, P, nk, producers)
@@ -295,7 +348,7 @@ def test_persistent_missing_stage_barrier_is_caught():
     ("loose_wait", False, 3), ("loose_wait", True, 3),
     ("no_barrier", False, 2), ("no_barrier", True, 3),
     ("slot_off", False, 3), ("slot_off", True, 2),
-    ("no_drain", False, 1),
+    ("no_drain", False, 1), ("no_drain", True, 2), ("no_drain", True, 4),
     ("steady_tail_wait", True, 3), ("steady_tail_wait", True, 4),
 ])
 def test_planted_schedule_mistake_is_caught(mut, producers, P):

@@ -510,6 +510,7 @@ struct TileCore {
     static_assert(WK == 1 || NWT * NREG * 256 <= LDS_BYTES, "LDS for the cross-group reduction");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 workgroup");
     static_assert(LOADS * (P > 0 ? P : 1) < 64, "vmcnt range");
+    static_assert(NP == 0 || LOADS * SLOTS < 64, "vmcnt range of the producer ring (SLOTS chunks in flight)");
 
     char *smem;
     uint32_t smem_base;
@@ -869,26 +870,29 @@ struct TileCore {
             }
         } else if constexpr (NP > 0) {
             if (nk <= 0) return;
-            // Producer / consumer ring (same slots, chunk order and barriers as
-            // below): after the barrier that ends chunk i - 1 the producers
-            // issue chunk i + P into the slot chunk i - 1 used, wait until
-            // chunk i + 2 has landed and meet the MFMA waves at the barrier
-            // that ends chunk i.
+            // Producer / consumer ring.  The MFMA waves meet the producers at
+            // k-step WIN of every chunk i, the point where their reads move
+            // from chunk i to chunk i + 1: at that barrier every read of slot
+            // i has completed (slot i is free) and chunk i + 1 has landed.
+            // Right after it the producers issue chunk i + SLOTS into slot i,
+            // so each chunk has P whole chunks of time to arrive (a barrier at
+            // the chunk's end, freeing the slot one read-ahead later and
+            // needing the chunk one read-ahead earlier, leaves P - 1).
             if (!mma) {
                 // Only real chunks are loaded (no zero fills past the last
                 // one: the MFMA waves' reads past the end are never used), so
                 // near the end fewer loads follow the chunk waited for.
 #pragma unroll
-                for (int c = 0; c < P; ++c)
+                for (int c = 0; c < SLOTS; ++c)
                     if (c < nk) issue(c_begin + c, c);
-                wait_chunks_after<P - 2>(min(P, nk) - 2);   // chunks 0 and 1 have landed
+                wait_chunks_after<P>(min(SLOTS, nk) - 1);   // chunk 0 has landed
                 block_barrier();
-                int fill = P;
+                int fill = 0;
                 for (int i = 0; i < nk; ++i) {
-                    if (i + P < nk) issue(c_begin + i + P, fill);
-                    // chunk i + 2 has landed (chunks up to i + P were issued)
-                    wait_chunks_after<P - 2>(min(i + P, nk - 1) - (i + 2));
-                    block_barrier();
+                    // chunk i + 1 has landed (chunks up to i + P were issued)
+                    wait_chunks_after<P - 1>(min(i + P, nk - 1) - (i + 1));
+                    block_barrier();   // k-step WIN of chunk i
+                    if (i + SLOTS < nk) issue(c_begin + i + SLOTS, fill);
                     fill = (fill + 1 == SLOTS) ? 0 : fill + 1;
                 }
                 wait_vmcnt<0>();
@@ -902,8 +906,11 @@ struct TileCore {
                 for (int i = 0; i < nk; ++i) {
                     const int next = (slot + 1 == SLOTS) ? 0 : slot + 1;
 #pragma unroll
-                    for (int ks = 0; ks < KSW; ++ks) step<FML>(ks, slot, next, 0, 0, false);
-                    block_barrier();
+                    for (int ks = 0; ks < KSW; ++ks) {
+                        // this wave's reads of slot i are complete; chunk i + 1 is in
+                        if (ks == WIN) lds_barrier();
+                        step<FML>(ks, slot, next, 0, 0, false);
+                    }
                     slot = next;
                 }
             }
@@ -1227,19 +1234,25 @@ struct TileCore {
     // tiles at W + k * PARTIAL_FLOATS (register order); tile `mine` (if
     // 0 <= mine < S) is taken from the accumulators themselves, which hold
     // exactly what was stored there.  MFMA waves only.
-    // the largest divisor of n that is at most 16 (register groups loaded per batch)
-    static constexpr int block_of(int n)
+    // the largest divisor of n that is at most `cap`
+    static constexpr int block_of(int n, int cap)
     {
-        int b = n < 16 ? n : 16;
+        int b = n < cap ? n : cap;
         while (n % b) --b;
         return b;
     }
+    // Register groups of 4 floats combined per batch: a batch holds 8 floats
+    // per group beside the accumulators (the running sum and the loaded
+    // partial).  With 128 accumulator floats per lane in VGPRs (a 64 x 128
+    // wave tile of 8 waves) 16 groups spilled 24 registers and 8 none; with
+    // 256 (accumulators in AGPRs) 16 spilled 3 and 8 spilled 160.
+    static constexpr int combine_batch() { return block_of(NREG / 4, NREG == 128 ? 8 : 16); }
 
     __device__ __forceinline__ void combine_l2(const float *W, int S, int mine)
     {
         if (!mma) return;
         constexpr int NQ = NREG / 4;
-        constexpr int QB = block_of(NQ);
+        constexpr int QB = combine_batch();
         static_assert(NQ % QB == 0, "register blocks");
         const __amdgpu_buffer_rsrc_t r = partial_rsrc(W);
 #pragma unroll
@@ -1298,7 +1311,7 @@ struct TileCore {
         // issued before any of them is used, so a piece costs one memory
         // round trip per block, not one per register group.
         constexpr int NQ = NREG / 4;
-        constexpr int QB = NQ < 16 ? NQ : 16;
+        constexpr int QB = combine_batch();
         static_assert(NQ % QB == 0, "register blocks");
 #pragma unroll
         for (int q0 = 0; q0 < NQ; q0 += QB) {

@@ -27,13 +27,16 @@ void register_f16(std::vector<ConfigEntry> &t, DtypeKernels &k)
     t.push_back(with_fixup<T, 128, 128, 128, 2, 2, 4, 32, 4>(with_persistent<T, 128, 128, 128, 2, 2, 4, 32, 3>(
         with_grouped<T, 128, 128, 128, 2, 2, 4, 32, 4>(make_entry_kp<T, 128, 128, 128, 2, 2, 1, 4, 32, 2, 3, 4>(
             d, 4, 0.42f, "f16 128x128 k64 waves2x2+4p mfma32")))));
-    t.push_back(make_entry_kp<T, 128, 128, 128, 2, 2, 1, 2, 32, 2, 3>(d, 3, 0.41f, "f16 128x128 k64 waves2x2+2p mfma32"));
+    t.push_back(make_entry_kp<T, 128, 128, 128, 2, 2, 1, 2, 32, 2>(d, 2, 0.41f, "f16 128x128 k64 waves2x2+2p mfma32"));
     // 96-column tiles, chosen only by configuration id (the bf16 table has the
     // measurements; f16 512 x 5632 x 2048: 17.6 vs 16.6 us on 128 x 128 + 4p)
     t.push_back(make_entry_kp<T, 128, 96, 128, 2, 2, 1, 4, 16, 2, 3, 4>(d, 4, 0.01f, "f16 128x96 k64 waves2x2+4p mfma16"));
-    t.push_back(make_entry_kp<T, 128, 256, 128, 2, 2, 1, 4, 32, 2>(d, 2, 0.36f, "f16 128x256 k64 waves2x2+4p mfma32"));
-    t.push_back(make_entry_kp<T, 256, 128, 128, 2, 2, 1, 4, 32, 2>(d, 2, 0.35f, "f16 256x128 k64 waves2x2+4p mfma32"));
-    t.push_back(make_entry_kp<T, 128, 256, 64, 2, 2, 1, 4, 32, 3, 4>(d, 4, 0.34f, "f16 128x256 k32 waves2x2+4p mfma32"));
+    t.push_back(with_fixup<T, 128, 256, 128, 2, 2, 4, 32, 2>(
+        make_entry_kp<T, 128, 256, 128, 2, 2, 1, 4, 32, 2>(d, 2, 0.36f, "f16 128x256 k64 waves2x2+4p mfma32")));
+    t.push_back(with_fixup<T, 256, 128, 128, 2, 2, 4, 32, 2>(
+        make_entry_kp<T, 256, 128, 128, 2, 2, 1, 4, 32, 2>(d, 2, 0.35f, "f16 256x128 k64 waves2x2+4p mfma32")));
+    t.push_back(with_fixup<T, 128, 256, 64, 2, 2, 4, 32, 4>(
+        make_entry_kp<T, 128, 256, 64, 2, 2, 1, 4, 32, 3, 4>(d, 4, 0.34f, "f16 128x256 k32 waves2x2+4p mfma32")));
     // k-groups: WK wave groups share each chunk's k-steps (fewer LDS reads per MFMA)
     //                    T  BM   BN   RB  waves WK MF  prefetch depths
     t.push_back(make_entry_k<T, 128, 128, 128, 2, 1, 2, 32, 2, 3>(d, 3, 0.4f, "f16 128x128 k64 waves2x1x2 mfma32"));
