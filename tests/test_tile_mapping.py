@@ -186,3 +186,16 @@ def test_fixup_plan_options():
     # (measured 15.1 against 16.0 us per call with the reduction kernel)
     p = gm.get_plan(128, 2048, 2048, 1, gm.F32, gm.EPI_RELU)
     assert p["fixup"] == 1 and p["split_k"] == 4
+
+
+@pytest.mark.parametrize("M,N,K,L,dtype", [(1000, 1100, 520, 1, "bf16"), (300, 200, 4096, 3, "f32")])
+def test_streamk_counters_one_line_per_tile(M, N, K, L, dtype):
+    """Stream-K keeps one counter per tile of all batches, each on its own
+    128-byte line (32 ints apart), followed by two partial tiles per workgroup."""
+    import tiled_dense_gemm_mkl_amd as gm
+
+    plan = gm.get_plan(M, N, K, L, gm.DTYPE_CODES[dtype], gm.EPI_RELU, gm.make_opts(streamk=True))
+    assert plan["streamk"] == 1
+    T = -(-M // plan["block_m"]) * -(-N // plan["block_n"]) * L
+    assert plan["counter_bytes"] == -(-T * 128 // 256) * 256
+    assert plan["workspace_bytes"] == plan["counter_bytes"] + 2 * plan["grid"] * plan["block_m"] * plan["block_n"] * 4

@@ -122,7 +122,7 @@ struct Plan {
     int32_t fix_per = 0;           // fix-up: tiles per XCD
     size_t fix_counter_bytes = 0;  // fix-up: per-tile counter words, 256-byte padded
     int64_t sk_units = 0;          // stream-K: tiles (all batches) * chunks per tile
-    size_t sk_counter_bytes = 0;   // stream-K: per-tile counters, 256-byte padded
+    size_t sk_counter_bytes = 0;   // stream-K: per-tile counters (one 128-byte line each), 256-byte padded
     int64_t grid = 0;
     int32_t tiles_m = 0, tiles_n = 0, group_m = 1;
     int32_t total_chunks = 0, chunks_per_split = 0;
@@ -490,7 +490,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
         plan->fixup = true;
         plan->fix_per = (int32_t)((tiles_all + 7) / 8);
         plan->grid = (int64_t)plan->fix_per * 8 * plan->S;
-        plan->fix_counter_bytes = ((size_t)tiles_all * kFixupCounterStride * 4 + 255) / 256 * 256;
+        plan->fix_counter_bytes = ((size_t)tiles_all * kCounterStride * 4 + 255) / 256 * 256;
         // [counters][partial tiles: S per tile]
         plan->ws_bytes = plan->fix_counter_bytes + (size_t)tiles_all * plan->S * c.bm * c.bn * 4;
     }
@@ -499,7 +499,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
         const int64_t tiles_all = (int64_t)plan->tiles_m * plan->tiles_n * L;
         plan->sk_units = tiles_all * total_chunks;
         plan->grid = streamk_grid(plan->sk_units, total_chunks);
-        plan->sk_counter_bytes = ((size_t)tiles_all * 4 + 255) / 256 * 256;
+        plan->sk_counter_bytes = ((size_t)tiles_all * kCounterStride * 4 + 255) / 256 * 256;
         // [counters][2 partial tiles per workgroup]
         plan->ws_bytes = plan->sk_counter_bytes + (size_t)2 * plan->grid * c.bm * c.bn * 4;
     }

@@ -1584,15 +1584,15 @@ __host__ __device__ __forceinline__ uint32_t fixup_map(const TileMap &m, int per
 struct FixupParams {
     TileParams t;            // split = S (2..6), chunks_per_split, map (tiles, S, raster)
     float *ws;               // [tiles of all batches][S] partial tiles
-    uint32_t *counters;      // one word per tile, kFixupCounterStride words apart, zero between calls
+    uint32_t *counters;      // one word per tile, kCounterStride words apart, zero between calls
     int32_t per;             // tiles per XCD: ceil(tiles of all batches / 8)
     int32_t force_remote;    // treat every other piece as not visible (recompute)
 };
 
 constexpr int kMaxFixupSplit = 6;
 // Counter words 128 bytes apart, one per cache line: the atomics of different
-// tiles then never queue behind each other on one line.
-constexpr int kFixupCounterStride = 32;
+// tiles then never queue behind each other on one line (fix-up and stream-K).
+constexpr int kCounterStride = 32;
 
 template <class T, int BM, int BN, int RB, int WAVES_M, int WAVES_N, int MF, int P, int MODE, int NP>
 __global__ __launch_bounds__((WAVES_M *WAVES_N + NP) * 64) void gemm_fixup_kernel(FixupParams fp)
@@ -1626,7 +1626,7 @@ __global__ __launch_bounds__((WAVES_M *WAVES_N + NP) * 64) void gemm_fixup_kerne
     if (threadIdx.x == 0) {
         const uint32_t me = xcc_id();
         const uint32_t add = 1u + ((me + 1u) << (8 + 4 * s));
-        uint32_t *cnt = fp.counters + (int64_t)v * kFixupCounterStride;
+        uint32_t *cnt = fp.counters + (int64_t)v * kCounterStride;
         const uint32_t old = __hip_atomic_fetch_add(cnt, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         uint32_t f = 0;
         if ((int)(old & 0xffu) == S - 1) {   // the last piece of the tile
@@ -1675,7 +1675,7 @@ __global__ __launch_bounds__((WAVES_M *WAVES_N + NP) * 64) void gemm_fixup_kerne
 struct StreamKParams {
     TileParams t;
     float *ws;        // 2 * gridDim.x partial tiles of BM * BN floats
-    int *counters;    // one per tile (all batches), zero between calls
+    int *counters;    // one per tile (all batches), kCounterStride ints apart, zero between calls
     int64_t units;    // tiles * total_chunks
 };
 
@@ -1724,7 +1724,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_streamk_kernel(Str
                 // a range's first piece goes to its slot 0, its last to slot 1
                 slots[k] = 2 * gk + ((range_start(U, gk, G) / C == tg) ? 0 : 1);
             }
-            int *cnt = sp.counters + tg;
+            int *cnt = sp.counters + tg * kCounterStride;
             // the piece that holds chunk 0 is normally the last to finish: if
             // every other piece is already in, it need not save its own
             bool last = false;
