@@ -403,7 +403,8 @@ def main() -> int:
     achieved = w.flops / (ev_ms_per_launch * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     kernel_config = gm.config_names()[plan["config_id"]] if plan["config_id"] >= 0 else "general"
-    kernel = f"{kernel_config} P{plan['prefetch_stages']} S{plan['split_k']}" + (" stream-K" if plan["streamk"] else "")
+    kernel = (f"{kernel_config} P{plan['prefetch_stages']} S{plan['split_k']}" + (" stream-K" if plan["streamk"] else "")
+              + (" fix-up" if plan.get("fixup") else ""))
     traffic = measured_traffic(key, kernel)
 
     result = {
