@@ -87,11 +87,15 @@ def schedule(KSW, NMF, NRD, LOADS, P, nk, producers=False, mut=None, tile_chunks
         ev.append(("wait", 0))
         return [ev], KSW * NMF, KSW * NRD
 
-    if not tile_chunks:
+    if not tile_chunks and P <= 3:
+        # (TileCore::WIN_MEET)
         return producer_ring(KSW, NMF, NRD, LOADS, P, nk, RA, NB, SLOTS, WIN, mut)
 
-    # producer waves load, MFMA waves read and compute.  The persistent ring
-    # keeps one load count per unit with zero fills.
+    # producer waves load, MFMA waves read and compute, and they meet at the
+    # end of every chunk.  The data-parallel producers load real chunks only
+    # and wait for exactly the loads that follow the chunk they need
+    # (wait_chunks_after); the persistent ring keeps one load count per unit
+    # with zero fills.
     def tail_wait(j):
         if mut == "steady_tail_wait":
             return WAIT
@@ -147,7 +151,7 @@ def schedule(KSW, NMF, NRD, LOADS, P, nk, producers=False, mut=None, tile_chunks
 
 
 def producer_ring(KSW, NMF, NRD, LOADS, P, nk, RA, NB, SLOTS, WIN, mut):
-    """The data-parallel producer ring: the producers issue every slot's
+    """The data-parallel producer ring at depth P <= 3: the producers issue every slot's
     chunk up front, and the MFMA waves meet them at k-step WIN of each chunk i
     (the barrier drains the MFMA waves' LDS reads): slot i is then free and
     chunk i + 1 has landed; right after it the producers issue chunk
@@ -348,7 +352,7 @@ def test_persistent_missing_stage_barrier_is_caught():
     ("loose_wait", False, 3), ("loose_wait", True, 3),
     ("no_barrier", False, 2), ("no_barrier", True, 3),
     ("slot_off", False, 3), ("slot_off", True, 2),
-    ("no_drain", False, 1), ("no_drain", True, 2), ("no_drain", True, 4),
+    ("no_drain", False, 1), ("no_drain", True, 2), ("no_drain", True, 3),
     ("steady_tail_wait", True, 3), ("steady_tail_wait", True, 4),
 ])
 def test_planted_schedule_mistake_is_caught(mut, producers, P):

@@ -497,6 +497,23 @@ struct TileCore {
     // and the barrier there also drains this wave's reads of chunk i (slot
     // i - 1 ... is refilled from the next chunk on).
     static constexpr int WIN = KSW - RA;
+    // Producer ring (NP > 0): where the MFMA waves meet the producers.
+    //   WIN_MEET (P <= 3): once per chunk at k-step WIN, where the MFMA waves'
+    //   reads move from chunk i to chunk i + 1; that barrier drains their LDS
+    //   reads, so slot i is free and chunk i + 1 must have landed.  Right
+    //   after it the producers issue chunk i + SLOTS into slot i: every chunk
+    //   has P chunk times to arrive.
+    //   Otherwise: once per chunk at its end, where every MFMA of chunk i is
+    //   issued (its reads of slot i have completed, no drain); the producers
+    //   then issue chunk i + P into the slot of chunk i - 1 and wait for chunk
+    //   i + 2 (whose first RA k-steps are read during chunk i + 1): P - 1
+    //   chunk times.
+    // Measured on 512 x 5632 x 2048 bf16 (interleaved, one box): depth 2 on
+    // 128 x 256 tiles 30.5 us at the chunk end against 21.4 us at WIN; depth 3
+    // on 128 x 192 20.2 against 20.0; depth 4 on 128 x 128 16.7 against
+    // 17.3 (and 1024 x 5632 x 8192: 99 against 102), where the drain at WIN
+    // costs more than the longer time to arrive gains.
+    static constexpr bool WIN_MEET = P <= 3;
     static constexpr int SPREAD = P >= 2 ? KSW : 1;
     static constexpr int LPK = (LOADS + SPREAD - 1) / SPREAD;      // loads per k-step
     static constexpr int WAIT_CNT = P >= 2 ? LOADS * (P - 2) : 0;
@@ -510,7 +527,7 @@ struct TileCore {
     static_assert(WK == 1 || NWT * NREG * 256 <= LDS_BYTES, "LDS for the cross-group reduction");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 workgroup");
     static_assert(LOADS * (P > 0 ? P : 1) < 64, "vmcnt range");
-    static_assert(NP == 0 || LOADS * SLOTS < 64, "vmcnt range of the producer ring (SLOTS chunks in flight)");
+    static_assert(NP == 0 || LOADS * (P + 1) < 64, "vmcnt range of the producer ring (up to P + 1 chunks in flight)");
 
     char *smem;
     uint32_t smem_base;
@@ -870,30 +887,38 @@ struct TileCore {
             }
         } else if constexpr (NP > 0) {
             if (nk <= 0) return;
-            // Producer / consumer ring.  The MFMA waves meet the producers at
-            // k-step WIN of every chunk i, the point where their reads move
-            // from chunk i to chunk i + 1: at that barrier every read of slot
-            // i has completed (slot i is free) and chunk i + 1 has landed.
-            // Right after it the producers issue chunk i + SLOTS into slot i,
-            // so each chunk has P whole chunks of time to arrive (a barrier at
-            // the chunk's end, freeing the slot one read-ahead later and
-            // needing the chunk one read-ahead earlier, leaves P - 1).
             if (!mma) {
                 // Only real chunks are loaded (no zero fills past the last
                 // one: the MFMA waves' reads past the end are never used), so
                 // near the end fewer loads follow the chunk waited for.
+                if constexpr (WIN_MEET) {
 #pragma unroll
-                for (int c = 0; c < SLOTS; ++c)
-                    if (c < nk) issue(c_begin + c, c);
-                wait_chunks_after<P>(min(SLOTS, nk) - 1);   // chunk 0 has landed
-                block_barrier();
-                int fill = 0;
-                for (int i = 0; i < nk; ++i) {
-                    // chunk i + 1 has landed (chunks up to i + P were issued)
-                    wait_chunks_after<P - 1>(min(i + P, nk - 1) - (i + 1));
-                    block_barrier();   // k-step WIN of chunk i
-                    if (i + SLOTS < nk) issue(c_begin + i + SLOTS, fill);
-                    fill = (fill + 1 == SLOTS) ? 0 : fill + 1;
+                    for (int c = 0; c < SLOTS; ++c)
+                        if (c < nk) issue(c_begin + c, c);
+                    wait_chunks_after<P>(min(SLOTS, nk) - 1);   // chunk 0 has landed
+                    block_barrier();
+                    int fill = 0;
+                    for (int i = 0; i < nk; ++i) {
+                        // chunk i + 1 has landed (chunks up to i + P were issued)
+                        wait_chunks_after<P - 1>(min(i + P, nk - 1) - (i + 1));
+                        block_barrier();   // k-step WIN of chunk i: slot i is free
+                        if (i + SLOTS < nk) issue(c_begin + i + SLOTS, fill);
+                        fill = (fill + 1 == SLOTS) ? 0 : fill + 1;
+                    }
+                } else {
+#pragma unroll
+                    for (int c = 0; c < P; ++c)
+                        if (c < nk) issue(c_begin + c, c);
+                    wait_chunks_after<P - 2>(min(P, nk) - 2);   // chunks 0 and 1 have landed
+                    block_barrier();
+                    int fill = P;
+                    for (int i = 0; i < nk; ++i) {
+                        if (i + P < nk) issue(c_begin + i + P, fill);   // into the slot of chunk i - 1
+                        // chunk i + 2 has landed (chunks up to i + P were issued)
+                        wait_chunks_after<P - 2>(min(i + P, nk - 1) - (i + 2));
+                        block_barrier();   // end of chunk i
+                        fill = (fill + 1 == SLOTS) ? 0 : fill + 1;
+                    }
                 }
                 wait_vmcnt<0>();
             } else {
@@ -908,9 +933,11 @@ struct TileCore {
 #pragma unroll
                     for (int ks = 0; ks < KSW; ++ks) {
                         // this wave's reads of slot i are complete; chunk i + 1 is in
-                        if (ks == WIN) lds_barrier();
+                        if (WIN_MEET && ks == WIN) lds_barrier();
                         step<FML>(ks, slot, next, 0, 0, false);
                     }
+                    // every MFMA of chunk i is issued, so its reads of slot i have completed
+                    if (!WIN_MEET) block_barrier();
                     slot = next;
                 }
             }
