@@ -154,7 +154,8 @@ int gemm_mkl(const void *A, const void *B, void *C,
  * automatic (for sweeps); GEMM_MKL_STREAMK=0/1/-1 never / always / by model
  * uses stream-K; GEMM_MKL_PERSISTENT=0/1/-1 never (default) / always / when
  * there are more tiles than compute units uses the persistent grid; GEMM_MKL_GROUP_M
- * sets the tile-raster group height;
+ * sets the tile-raster group height (default 4; 6 inside the groups of
+ * gemm_mkl_grouped);
  * GEMM_MKL_LOG=1 prints each call's plan to stderr;
  * GEMM_MKL_WORKSPACE_LIMIT=<bytes> caps the internal workspace.  They are
  * read once, at the first call.  Plans are cached per (sizes, dtype, pointer

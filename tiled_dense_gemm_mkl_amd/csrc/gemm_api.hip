@@ -79,13 +79,18 @@ int env_int(const char *name, int dflt)
 
 // The environment overrides, read once, at the first call that needs them.
 struct EnvSettings {
-    int force_config, stages, split_k, streamk, group_m, log, persistent, fixup;
+    int force_config, stages, split_k, streamk, group_m, grouped_group_m, log, persistent, fixup;
     bool has_ws_limit;
     size_t ws_limit;
     EnvSettings()
         : force_config(env_int("GEMM_MKL_FORCE_CONFIG", -1)), stages(env_int("GEMM_MKL_STAGES", -1)),
           split_k(env_int("GEMM_MKL_SPLIT_K", 0)), streamk(env_int("GEMM_MKL_STREAMK", 0)),
-          group_m(env_int("GEMM_MKL_GROUP_M", 4)), log(env_int("GEMM_MKL_LOG", 0)),
+          group_m(env_int("GEMM_MKL_GROUP_M", 4)),
+          // the grouped kernel's raster height inside a group: on 4096 rows in
+          // 8 groups x 5632 x 2048 bf16 (256 x 256 tiles) heights 1, 2, 3, 4,
+          // 6, 8 and 16 read FETCH_SIZE 217, 169, 144, 145, 140, 148 and 142
+          // thousand KiB per call, at 104-110 us per call
+          grouped_group_m(env_int("GEMM_MKL_GROUP_M", 6)), log(env_int("GEMM_MKL_LOG", 0)),
           persistent(env_int("GEMM_MKL_PERSISTENT", 0)), fixup(env_int("GEMM_MKL_FIXUP", -1)), has_ws_limit(false),
           ws_limit(0)
     {
@@ -930,7 +935,7 @@ int run_grouped(const void *A, const void *B, void *C, const int32_t *offs, int6
     gp.tiles_n = (int32_t)tiles_n;
     gp.row_tiles = (int32_t)row_tiles;
     gp.total_chunks = (int32_t)((Kp * es + c.rb - 1) / c.rb);
-    gp.group_m = std::max<int32_t>(1, (int32_t)env().group_m);
+    gp.group_m = std::max<int32_t>(1, (int32_t)env().grouped_group_m);
     if (env().log)
         std::fprintf(stderr, "gemm_mkl_grouped: G=%lld rows=%lld N=%lld K=%lld dtype=%d epi=%d -> %s P=%d grid=%lld\n",
                      (long long)G, (long long)total_m, (long long)N, (long long)K, dtype, epilogue, c.name,
