@@ -181,3 +181,46 @@ def test_grouped_empty_problems_launch_nothing():
     for args in [(0, 8, 8, 64), (3, 0, 8, 64), (3, 8, 0, 64)]:
         G, total_m, N, K = args
         assert gm.gemm_mkl_grouped(None, None, None, None, G, total_m, N, K, gm.BF16, gm.EPI_RELU, None, None) == 0
+
+
+def _cid(name):
+    return gm.config_names().index(name)
+
+
+@pytest.mark.parametrize("cfg", ["bf16 256x256 k64 waves2x4 mfma32", "bf16 256x256 k32 waves2x2 mfma32",
+                                 "bf16 128x128 k64 waves2x2+4p mfma32", "bf16 64x64 k64 waves2x2 mfma32"])
+def test_grouped_last_tile_every_live_block_count(orc, cfg):
+    """A group's last tile computes only its row blocks that hold rows, shared
+    out over the wave rows: groups whose last tile holds 1..8 blocks of 32
+    rows (and one more row than a block boundary, or one fewer) run through
+    every such count, bit for bit on integer inputs, within the tolerance on
+    random ones; rows of no group stay untouched."""
+    dtype = "bf16"
+    sizes = [32 * b - 1 for b in range(1, 9)] + [256 + 32 * b + 1 for b in range(0, 8)] + [512]
+    offs = np.cumsum(sizes).astype(np.int32)
+    total_m, G, N, K = int(offs[-1]) + 5, len(sizes), 136, 256
+    A, B = _operands(dtype, total_m, G, N, K, seed=21)
+    Ai, Bi = _operands(dtype, total_m, G, N, K, seed=22, integer=True)
+    cid = _cid(cfg)
+    C = _run(A, B, offs, dtype, "relu", config_id=cid)
+    _check(C, orc.gemm_grouped64(A, B, offs, dtype, "relu"), A, B, dtype, K, cfg)
+    Ci = _run(Ai, Bi, offs, dtype, "relu", config_id=cid)
+    refi = orc.round_to_dtype(orc.gemm_grouped64(Ai, Bi, offs, dtype, "relu"), dtype)
+    covered = ~np.isnan(orc.gemm_grouped64(Ai, Bi, offs, dtype, "relu")[:, 0])
+    assert_bits_equal(Ci[covered], refi[covered], f"integer {cfg}")
+
+
+def test_grouped_many_groups_take_the_remapped_grid(orc):
+    """More than 512 groups: the workgroups skip the exact tile count and map
+    their ids over the whole grid instead (ids past the last tile exit)."""
+    dtype = "bf16"
+    rng = np.random.default_rng(31)
+    sizes = rng.integers(0, 9, size=700)
+    offs = np.cumsum(sizes).astype(np.int32)
+    total_m, G, N, K = int(offs[-1]), len(sizes), 72, 64
+    A, B = _operands(dtype, total_m, G, N, K, seed=32)
+    C = _run(A, B, offs, dtype, "identity")
+    _check(C, orc.gemm_grouped64(A, B, offs, dtype, "identity"), A, B, dtype, K, "700 groups")
+    Ai, Bi = _operands(dtype, total_m, G, N, K, seed=33, integer=True)
+    refi = orc.round_to_dtype(orc.gemm_grouped64(Ai, Bi, offs, dtype, "identity"), dtype)
+    assert_bits_equal(_run(Ai, Bi, offs, dtype, "identity"), refi, "700 groups integer")
