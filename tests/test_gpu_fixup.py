@@ -43,6 +43,8 @@ CASES = [
     ("f32", 128, 2048, 2048, 1, 4, "f32 64x64 k32 waves2x2 mfma16"),
     ("f32", 100, 300, 520, 3, 3, "f32 64x64 k32 waves2x2 mfma16"),
     ("f32", 200, 200, 1024, 1, 2, "f32 128x128 k32 waves2x2 mfma32"),
+    ("f32", 128, 2048, 2048, 1, 4, "f32 64x64 k32 waves2x2+4p mfma16"),
+    ("f32", 100, 300, 520, 3, 3, "f32 64x64 k32 waves2x2+4p mfma16"),
 ]
 
 

@@ -483,13 +483,14 @@ struct TileCore {
     static constexpr int RA = (NMF >= 8 || KSW < 4) ? 1 : KSW - 1;
     static constexpr int NB = RA + 1;
     static_assert(KSW % NB == 0, "fragment ring must divide a wave's k-steps of a chunk");
-    // P >= 2: one wait and one barrier per chunk, at the chunk boundary.  At
+    // Every wave loads (NP == 0), P >= 2: one wait and one barrier per chunk,
+    // at the chunk boundary.  At
     // the end of chunk i every wave has issued all MFMAs of chunk i (so its
     // reads of slot i are complete) and chunk i + 2 must be visible (its first
     // RA k-steps are read during chunk i + 1); the loads of chunk i + 1 + P,
     // spread over all k-steps of chunk i + 1, then refill slot i.  In flight
     // at the wait: the loads of chunks i + 3 .. i + P.
-    // P == 1: chunk i + 1 is loaded during chunk i itself, so it is waited for
+    // NP == 0, P == 1: chunk i + 1 is loaded during chunk i itself, so it is waited for
     // at k-step WIN = KSW - RA of chunk i, just before its first reads; the
     // loads all go out in k-step 0, between its MFMAs, to give them the most
     // time before the wait (measured against spreading them over the k-steps

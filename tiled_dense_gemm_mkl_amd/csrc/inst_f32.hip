@@ -25,6 +25,13 @@ void register_f32(std::vector<ConfigEntry> &t, DtypeKernels &k)
     t.push_back(with_fixup<T, 64, 64, 128, 2, 2, 0, 16, 3>(
         make_entry<T, 64, 64, 128, 2, 2, 16, 1, 2, 3, 4>(d, 3, 0.401f, "f32 64x64 k32 waves2x2 mfma16")));
     t.push_back(make_entry<T, 32, 64, 128, 1, 2, 16, 1, 2, 3>(d, 2, 0.25f, "f32 32x64 k32 waves1x2 mfma16"));
+    // four producer waves beside the 64 x 64 tile's four MFMA waves: faster
+    // than the same tile without them on every fp32 shape measured
+    // (128x2048x2048 S=4 with the in-kernel fix-up 13.2-13.6 against
+    // 14.9-15.3 us, 256x1024x1024 9.7 against 10.5, 2048^3 127 against 135,
+    // 4096^3 985 against 1047 (1029 on 128 x 128))
+    t.push_back(with_fixup<T, 64, 64, 128, 2, 2, 4, 16, 3>(
+        make_entry_kp<T, 64, 64, 128, 2, 2, 1, 4, 16, 2, 3, 4>(d, 3, 0.43f, "f32 64x64 k32 waves2x2+4p mfma16")));
     fill_dtype_kernels<T>(k);
 }
 
