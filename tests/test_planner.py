@@ -89,3 +89,35 @@ def test_opt_in_tile_is_never_chosen_but_can_be_forced():
 def test_grouped_tile_follows_group_size(G, rows, want):
     cid = gm.grouped_config(G, G * rows, 5632, 2048, gm.BF16, gm.EPI_RELU)
     assert gm.config_names()[cid] == want
+
+
+# bf16 shapes of the planner audit (graph replay, one box) whose automatic plan
+# changed with the 64 x 64 producer tile, the 128 x 256 producer tile's figure
+# and the rule that 16-bit plans take the in-kernel fix-up only when forced
+AUDITED = {
+    (1024, 1024, 4096): ("bf16 64x64 k64 waves2x2+4p mfma32", 1),      # 17.6 us (four fix-up pieces of 128 x 128: 22.7)
+    (256, 4096, 4096): ("bf16 64x64 k64 waves2x2+4p mfma32", 1),       # 17.3 us (22.7)
+    (512, 2048, 2048): ("bf16 64x64 k64 waves2x2+4p mfma32", 1),       # 9.9 us (64 x 64 without producers 10.7)
+    (128, 5632, 2048): ("bf16 64x64 k64 waves2x2+4p mfma32", 1),       # 9.3 us (9.8)
+    (1024, 8192, 8192): ("bf16 128x256 k64 waves2x2+4p mfma32", 1),    # 111-112 us (two fix-up pieces of 256 x 256: 131.7)
+    (1024, 8192, 2048): ("bf16 128x256 k64 waves2x2+4p mfma32", 1),    # 32.3 us (256 x 128: 37.5)
+    (4096, 8192, 2048): ("bf16 256x256 k64 waves2x4 mfma32", 1),       # 116-118 us (128 x 256: 124.2)
+    (256, 5632, 512): ("bf16 64x64 k64 waves2x2 mfma32", 1),           # two per CU: 5.70 us (with producers 5.89)
+}
+
+
+@pytest.mark.parametrize("shape", sorted(AUDITED))
+def test_audited_bf16_plans(shape):
+    p = _plan(*shape, 1, "bf16")
+    assert (gm.config_names()[p["config_id"]], p["split_k"]) == AUDITED[shape]
+    assert p["fixup"] == 0
+
+
+def test_16bit_fixup_only_when_forced():
+    """The in-kernel fix-up is never chosen automatically for 16-bit types
+    (no shape measured it faster than the best plan without it), but a forced
+    split or a forced fix-up still takes it."""
+    for M, N, K in [(256, 8192, 2048), (1024, 8192, 8192), (1024, 1024, 4096), (512, 3584, 18944)]:
+        assert _plan(M, N, K, 1, "bf16")["fixup"] == 0
+    assert _plan(512, 5632, 2048, 1, "bf16", split_k=2, fixup=True)["fixup"] == 1
+    assert _plan(512, 5632, 2048, 1, "bf16", split_k=2)["fixup"] == 1

@@ -199,8 +199,16 @@ double model_cycles(const ConfigEntry &c, int dtype, int64_t M, int64_t N, int64
     // workgroups per CU through a split for K = 4096 (1024 x 1024 x 4096: 72.7
     // against 78.4 us); below 0.9 it would pick 8 splits for 128 x 2048 x 2048,
     // measured slower than 4.
+    // 16-bit tiles with producer waves gain nothing from a second workgroup
+    // on the CU: bf16 64 x 64 with four producers ran 3-5% slower than without
+    // them at 352..512 tiles (two per CU: 256 x 5632 x 512 5.89 against 5.70
+    // us, 256 x 8192 x 512 6.25 against 5.95) but 6-8% faster at 176..256
+    // tiles (128 x 5632 x 2048 9.28 against 9.84, 512 x 2048 x 2048 9.85
+    // against 10.69).  fp32's producer tile did gain (1024 x 1024 x 4096 two
+    // splits, two per CU, 67.6 us, within 1% of its best).
+    const bool can_share = !(c.producers > 0 && dtype != GEMM_MKL_F32);
     int64_t w = 1;
-    if (p >= 0 && 2 * (int64_t)(c.bm + c.bn) * c.rb * (p + 1) <= 160 * 1024)
+    if (can_share && p >= 0 && 2 * (int64_t)(c.bm + c.bn) * c.rb * (p + 1) <= 160 * 1024)
         w = std::min<int64_t>(2, (units + kNumCUs - 1) / kNumCUs);
     const int64_t rounds = (units + kNumCUs * w - 1) / (kNumCUs * w);
     const double share = w > 1 ? (dtype == GEMM_MKL_F32 ? 0.95 : 0.8) * (double)w : 1.0;
@@ -449,8 +457,18 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t L, int dtype, const gemm_
                 }
             }
             const int64_t tiles_all = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn) * L;
+            // 16-bit plans take the fix-up only when it or the split is
+            // forced: no 16-bit shape measured faster with it than with the
+            // best plan without it, and the model ranked it first where it
+            // lost (bf16, graph replay: 256 x 8192 x 2048 two pieces 20.0 us
+            // against 15.3 on 128 x 128 unsplit; 1024 x 8192 x 8192 two pieces
+            // of 256 x 256 131.7 against 111.1 on 128 x 256 unsplit;
+            // 1024 x 1024 x 4096 four pieces 22.7 against 17.6 on 64 x 64;
+            // the K-heavy L=8 shape two pieces 585 against 547 unsplit).  fp32
+            // takes it by the model (128 x 2048 x 2048: 13.4 us, four pieces).
+            const bool fix_s_ok = fix_mode == 1 || forced_s > 0 || dtype == GEMM_MKL_F32;
             const bool fix_ok = S > 1 && fix_mode != 0 && c.fixup[0] != nullptr && S <= kMaxFixupSplit &&
-                                p == c.default_p && tiles_all <= kMaxFixupTiles &&
+                                fix_s_ok && p == c.default_p && tiles_all <= kMaxFixupTiles &&
                                 (ws_cap == 0 || (double)tiles_all * S * c.bm * c.bn * 4.0 <= (double)ws_cap);
             if (fix_ok) {
                 const double cyc = model_cycles(c, dtype, M, N, K, L, S, p, true);

@@ -37,7 +37,7 @@ void register_bf16(std::vector<ConfigEntry> &t, DtypeKernels &k)
     // 16 x 16 MFMAs: a 2 x 2 wave grid of 64 x 48.
     t.push_back(make_entry_kp<T, 128, 96, 128, 2, 2, 1, 4, 16, 2, 3, 4>(d, 4, 0.01f, "bf16 128x96 k64 waves2x2+4p mfma16"));
     t.push_back(with_fixup<T, 128, 256, 128, 2, 2, 4, 32, 2>(
-        make_entry_kp<T, 128, 256, 128, 2, 2, 1, 4, 32, 2>(d, 2, 0.36f, "bf16 128x256 k64 waves2x2+4p mfma32")));
+        make_entry_kp<T, 128, 256, 128, 2, 2, 1, 4, 32, 2>(d, 2, 0.46f, "bf16 128x256 k64 waves2x2+4p mfma32")));
     t.push_back(with_fixup<T, 256, 128, 128, 2, 2, 4, 32, 2>(
         make_entry_kp<T, 256, 128, 128, 2, 2, 1, 4, 32, 2>(d, 2, 0.35f, "bf16 256x128 k64 waves2x2+4p mfma32")));
     t.push_back(with_fixup<T, 128, 256, 64, 2, 2, 4, 32, 4>(
@@ -66,6 +66,7 @@ void register_bf16(std::vector<ConfigEntry> &t, DtypeKernels &k)
     t.push_back(make_entry_kp<T, 128, 128, 64, 2, 2, 1, 4, 32, 4, 6, 8>(d, 6, 0.30f, "bf16 128x128 k32 waves2x2+4p mfma32"));
     t.push_back(with_fixup<T, 128, 192, 64, 2, 2, 4, 32, 6>(
         make_entry_kp<T, 128, 192, 64, 2, 2, 1, 4, 32, 4, 6, 7>(d, 6, 0.30f, "bf16 128x192 k32 waves2x2+4p mfma32")));
+    t.push_back(make_entry_kp<T, 64, 64, 128, 2, 2, 1, 4, 32, 2, 3, 4>(d, 3, 0.26f, "bf16 64x64 k64 waves2x2+4p mfma32"));
     fill_dtype_kernels<T>(k);
 }
 
