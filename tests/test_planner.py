@@ -10,7 +10,7 @@ from tiled_dense_gemm_mkl_amd import workloads
 
 # plans measured best (or within timing noise) on MI355X for each workload
 NAMED = {
-    "bf16_512x5632x2048_relu": ("bf16 128x128 k64 waves2x2+4p mfma32", 4, 1),
+    "bf16_512x5632x2048_relu": ("bf16 128x128 k64 waves2x2+4p mfma16", 3, 1),
     "f16_8192x8192x8192_identity": ("f16 256x256 k64 waves2x4 mfma32", 1, 1),
     "bf16_L8_512x3584x18944_silu": ("bf16 256x256 k32 waves2x2 mfma32", 4, 1),
     "f32_128x2048x2048_relu": ("f32 64x64 k32 waves2x2+4p mfma16", 3, 4),
@@ -95,12 +95,12 @@ def test_grouped_tile_follows_group_size(G, rows, want):
 # changed with the 64 x 64 producer tile, the 128 x 256 producer tile's figure
 # and the rule that 16-bit plans take the in-kernel fix-up only when forced
 AUDITED = {
-    (1024, 1024, 4096): ("bf16 64x64 k64 waves2x2+4p mfma32", 1),      # 17.6 us (four fix-up pieces of 128 x 128: 22.7)
-    (256, 4096, 4096): ("bf16 64x64 k64 waves2x2+4p mfma32", 1),       # 17.3 us (22.7)
-    (512, 2048, 2048): ("bf16 64x64 k64 waves2x2+4p mfma32", 1),       # 9.9 us (64 x 64 without producers 10.7)
-    (128, 5632, 2048): ("bf16 64x64 k64 waves2x2+4p mfma32", 1),       # 9.3 us (9.8)
-    (1024, 8192, 8192): ("bf16 128x256 k64 waves2x2+4p mfma32", 1),    # 111-112 us (two fix-up pieces of 256 x 256: 131.7)
-    (1024, 8192, 2048): ("bf16 128x256 k64 waves2x2+4p mfma32", 1),    # 32.3 us (256 x 128: 37.5)
+    (1024, 1024, 4096): ("bf16 64x64 k64 waves2x2+4p mfma16", 1),      # 15.6 us; 32 x 32 MFMAs 17.2-17.6 (four fix-up pieces of 128 x 128: 22.7)
+    (256, 4096, 4096): ("bf16 64x64 k64 waves2x2+4p mfma16", 1),       # 32 x 32 MFMAs 17.3 us (22.7)
+    (512, 2048, 2048): ("bf16 64x64 k64 waves2x2+4p mfma16", 1),       # 9.2 us (32 x 32 MFMAs 9.5, no producers 10.7)
+    (128, 5632, 2048): ("bf16 64x64 k64 waves2x2+4p mfma16", 1),       # 32 x 32 MFMAs 9.3 us (9.8)
+    (1024, 8192, 8192): ("bf16 128x256 k64 waves2x2+4p mfma16", 1),    # 101.8 us; 32 x 32 MFMAs 109-112 (two fix-up pieces of 256 x 256: 131.7)
+    (1024, 8192, 2048): ("bf16 128x256 k64 waves2x2+4p mfma16", 1),    # 31.0 us; 32 x 32 MFMAs 32.2 (256 x 128: 37.5)
     (4096, 8192, 2048): ("bf16 256x256 k64 waves2x4 mfma32", 1),       # 116-118 us (128 x 256: 124.2)
     (256, 5632, 512): ("bf16 64x64 k64 waves2x2 mfma32", 1),           # two per CU: 5.70 us (with producers 5.89)
 }

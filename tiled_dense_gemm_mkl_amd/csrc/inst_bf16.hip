@@ -67,6 +67,17 @@ void register_bf16(std::vector<ConfigEntry> &t, DtypeKernels &k)
     t.push_back(with_fixup<T, 128, 192, 64, 2, 2, 4, 32, 6>(
         make_entry_kp<T, 128, 192, 64, 2, 2, 1, 4, 32, 4, 6, 7>(d, 6, 0.30f, "bf16 128x192 k32 waves2x2+4p mfma32")));
     t.push_back(make_entry_kp<T, 64, 64, 128, 2, 2, 1, 4, 32, 2, 3, 4>(d, 3, 0.26f, "bf16 64x64 k64 waves2x2+4p mfma32"));
+    // The producer tiles on 16 x 16 MFMAs: faster than on 32 x 32 in every
+    // interleaved A/B (graph replay, bf16 unless noted): 128 x 128 on
+    // 512x5632x2048 15.05 us at depth 3 against 15.54 at depth 4 (fp16 16.17
+    // against 16.36), 1024x5632x8192 95.9 against 97.2, 2048^3 17.5 against
+    // 18.0; 128 x 256 on 1024x8192x2048 31.0 against 32.2, 1024x8192x8192
+    // 101.8 against 109.4; 64 x 64 on 1024x1024x4096 15.6 against 17.2,
+    // 512x2048x2048 9.20 against 9.51.  Their figures sit just above the
+    // 32 x 32 variants', which keep the fix-up and grouped kernels.
+    t.push_back(make_entry_kp<T, 128, 128, 128, 2, 2, 1, 4, 16, 3, 4>(d, 3, 0.43f, "bf16 128x128 k64 waves2x2+4p mfma16"));
+    t.push_back(make_entry_kp<T, 128, 256, 128, 2, 2, 1, 4, 16, 2>(d, 2, 0.47f, "bf16 128x256 k64 waves2x2+4p mfma16"));
+    t.push_back(make_entry_kp<T, 64, 64, 128, 2, 2, 1, 4, 16, 3>(d, 3, 0.27f, "bf16 64x64 k64 waves2x2+4p mfma16"));
     fill_dtype_kernels<T>(k);
 }
 
