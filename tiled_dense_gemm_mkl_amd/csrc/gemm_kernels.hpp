@@ -996,7 +996,7 @@ struct TileCore {
     }
 
     // run() for a tile whose first `live` rows exist (live <= BM): each MFMA
-    // wave computes only its fragment rows that start above row `live`
+    // wave computes only its fragment rows that start before row `live`
     // (interleaved rows: every wave row gets its share of the live blocks).
     // The loads, waits and barriers are those of run() for every wave.
     template <bool FRESH = false>
@@ -1440,7 +1440,8 @@ struct GroupedParams {
 // workgroup reaches the same answer.  Offsets are clamped to a non-decreasing
 // sequence in [0, total_m], so no offsets can address rows outside A or C.
 // With tr < 0 nothing is looked up: the scan runs over every group and
-// returns the total number of row tiles (g stays -1).
+// returns the total number of row tiles (g stays -1); with tr >= 0 the
+// return value is not meaningful.
 template <int BM>
 __device__ __forceinline__ int find_group(const GroupedParams &gp, int tr, int &g, int &tm, int &row0, int &rows)
 {
