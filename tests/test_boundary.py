@@ -474,3 +474,19 @@ def test_noalloc_argument_checks(lib):
     assert call(512, 4096, 2048, 1, BF16, ID, gm.make_opts(split_k=16)) == -4
     # repacked operands that exceed it (K = 2047 bf16: A and B copied, 2 * 4096 * 2048 * 2 B each)
     assert call(4096, 4096, 2047, 2, BF16, ID, None) == -4
+
+
+def test_library_shares_torchs_hip_runtime():
+    # regression: the library loaded before torch bound the system HIP runtime
+    # while torch brought its own, and GPU calls then found no device; load()
+    # imports torch first so that one runtime serves both
+    import subprocess
+    import sys
+
+    code = ("import os, tiled_dense_gemm_mkl_amd as gm; gm.config_names(); import torch; "
+            "maps = open('/proc/self/maps').read(); "
+            "print(len({l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l}))")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=root, timeout=300)
+    assert out.returncode == 0, out.stderr[-2000:]
+    assert out.stdout.strip().splitlines()[-1] == "1"

@@ -112,6 +112,12 @@ def load(path: str = LIB_PATH):
         raise ImportError(
             f"{path} is missing: build the HIP library first "
             "(python -m tiled_dense_gemm_mkl_amd.build); there is no fallback path")
+    # torch's wheel carries its own HIP runtime.  Loaded first, it is the copy
+    # this library binds to (same soname); loaded after this library, it
+    # comes in beside the system runtime that this library would then have
+    # bound, and two runtimes in one process share no devices, streams or
+    # memory (calls then fail with "no ROCm-capable device").
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
     lib.gemm_mkl.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i32, vp]
