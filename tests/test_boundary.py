@@ -490,3 +490,20 @@ def test_library_shares_torchs_hip_runtime():
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=root, timeout=300)
     assert out.returncode == 0, out.stderr[-2000:]
     assert out.stdout.strip().splitlines()[-1] == "1"
+
+
+def test_workspace_tensor_must_be_on_the_operands_gpu():
+    # regression: gemm() passed any workspace tensor's address to the kernels,
+    # so one in host memory would have been written by the GPU at a host address
+    import torch
+
+    gpu = torch.device("cuda", 0)
+    assert gm._binding._workspace_args(None, gpu) == (None, 0)
+    with pytest.raises(ValueError, match="workspace"):
+        gm._binding._workspace_args(torch.zeros(64), gpu)
+    with pytest.raises(ValueError, match="workspace"):
+        gm._binding._workspace_args(torch.zeros(8, 8).t(), torch.device("cpu"))
+    with pytest.raises(TypeError, match="workspace"):
+        gm._binding._workspace_args(bytearray(64), gpu)
+    ptr, nbytes = gm._binding._workspace_args(torch.zeros(64, dtype=torch.float64), torch.device("cpu"))
+    assert nbytes == 512 and ptr != 0

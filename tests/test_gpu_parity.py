@@ -256,6 +256,11 @@ def test_workspace_too_small_is_rejected_and_C_untouched():
     assert e.value.status == -4
     torch.cuda.synchronize()
     assert torch.all(c == 3.0).item()
+    # a workspace in host memory is refused before any launch
+    with pytest.raises(ValueError, match="workspace"):
+        gm.gemm(a, b, "relu", out=c, split_k=2, workspace=torch.zeros(1 << 20))
+    torch.cuda.synchronize()
+    assert torch.all(c == 3.0).item()
 
 
 def test_non_default_stream(orc):

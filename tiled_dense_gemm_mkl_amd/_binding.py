@@ -304,6 +304,24 @@ def _torch_dtype_code(t) -> int:
     return codes[t.dtype]
 
 
+def _workspace_args(workspace, device):
+    """(pointer, bytes) of a caller workspace tensor, or (None, 0) for none.
+
+    The kernels write the workspace at its raw address, so a tensor in host
+    memory or on another GPU would be an invalid device access: it is
+    rejected here, as is one whose bytes are not contiguous.
+    """
+    import torch
+
+    if workspace is None:
+        return None, 0
+    if not isinstance(workspace, torch.Tensor):
+        raise TypeError("workspace must be a torch tensor")
+    if workspace.device != device or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}, got one on {workspace.device}")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
 def gemm(a, b, epilogue: str = "identity", out=None, *, prefetch_stages=None, split_k=None,
          config_id=None, force_general=False, workspace=None, stream=None, streamk=None, persistent=None,
          fixup=None, fixup_recompute=False):
@@ -344,9 +362,7 @@ def gemm(a, b, epilogue: str = "identity", out=None, *, prefetch_stages=None, sp
         if tuple(out3.shape) != (L, M, N) or out3.dtype != a.dtype or not out3.is_contiguous() \
                 or out3.device != a.device:
             raise ValueError("out must be a contiguous [L, M, N] tensor of the operand dtype on the same GPU")
-    ws_ptr = ws_bytes = None
-    if workspace is not None:
-        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    ws_ptr, ws_bytes = _workspace_args(workspace, a.device)
     opts = make_opts(prefetch_stages, split_k, config_id, force_general, ws_ptr, ws_bytes or 0, streamk, persistent,
                      fixup, fixup_recompute)
     s = stream if stream is not None else torch.cuda.current_stream(a.device)
