@@ -20,7 +20,9 @@
  * to the output dtype (round to nearest even).
  *
  * Pointers: A, B, C are DEVICE pointers owned by the caller; the library never
- * allocates, frees or retains them.  C must not overlap A or B.  Each base
+ * allocates, frees or retains them.  C must share no byte with A or B (a C
+ * that does is INVALID_VALUE, checked on the addresses before any launch; A
+ * and B may overlap each other, both are only read).  Each base
  * pointer must be aligned to its element size.  The tile kernels read A and B
  * in 16-byte pieces: when K*sizeof(element) is not a multiple of 16, or A or
  * B is not 16-byte aligned, the call first copies the operand(s) into rows of
@@ -71,6 +73,8 @@ enum {
     GEMM_MKL_STATUS_INVALID_VALUE = -1,        /* null pointer for a non-empty problem,
                                                   negative size, size overflow,
                                                   pointer not aligned to its element,
+                                                  an output sharing bytes with an
+                                                  input or the workspace,
                                                   prefetch_stages < -1, bad option */
     GEMM_MKL_STATUS_UNSUPPORTED_DTYPE = -2,    /* dtype not one of GEMM_MKL_F32/F16/BF16 */
     GEMM_MKL_STATUS_UNSUPPORTED_EPILOGUE = -3, /* epilogue not one of GEMM_MKL_EPI_* */
@@ -143,7 +147,8 @@ int gemm_mkl(const void *A, const void *B, void *C,
  *   internal workspace).  It must hold the plan's workspace_bytes
  *   (gemm_mkl_get_plan, which assumes 16-byte aligned pointers: a misaligned
  *   A or B also needs its repacked copy, L * rows * Kp * element bytes
- *   rounded up to 256) and be 256-byte aligned; too small is
+ *   rounded up to 256) and be 256-byte aligned, sharing no byte with A, B
+ *   or C (INVALID_VALUE otherwise); too small is
  *   GEMM_MKL_STATUS_WORKSPACE, before anything is launched.  A stream-K or
  *   fix-up plan uses its first plan.counter_bytes bytes as per-tile counters:
  *   they must be zero before the first such call with that workspace, and
@@ -263,7 +268,8 @@ int gemm_mkl_noalloc(const void *A, const void *B, void *C,
  *
  * Returns GEMM_MKL_STATUS_OK (also for G, total_m or N equal to 0: no
  * launch), INVALID_VALUE (negative sizes, G > 65536, total_m >= 2^31, null or
- * element-misaligned pointers), UNSUPPORTED_DTYPE / _EPILOGUE, WORKSPACE (a
+ * element-misaligned pointers, a C or caller workspace sharing bytes with
+ * another argument), UNSUPPORTED_DTYPE / _EPILOGUE, WORKSPACE (a
  * caller workspace too small for the repacked operands), NOT_AVAILABLE (no
  * configuration fits) or HIP_ERROR.  Ownership as for gemm_mkl.
  */
@@ -282,7 +288,7 @@ int gemm_mkl_grouped(const void *A, const void *B, void *C, const int32_t *offs,
  * x:      device pointer, [rows][hidden], hidden contiguous.
  * weight: device pointer to hidden elements, or NULL for no weight (y = x * rsqrt(...)).
  * y:      device pointer, [rows][hidden]; may equal x (in place); any other
- *         overlap with x or weight is undefined.
+ *         byte shared with x or weight is INVALID_VALUE.
  * x, weight and y share dtype (GEMM_MKL_F32/F16/BF16); the sum, rsqrt and
  * products run in fp32 and the result is rounded once (round to nearest even)
  * to the dtype.  eps must be finite and >= 0.  The squares are summed in an
@@ -292,7 +298,7 @@ int gemm_mkl_grouped(const void *A, const void *B, void *C, const int32_t *offs,
  * Returns GEMM_MKL_STATUS_OK (also for rows or hidden equal to 0: no launch),
  * INVALID_VALUE (negative sizes, hidden >= 2^31, size overflow, eps negative,
  * NaN or infinite, null x or y for a non-empty problem, element-misaligned
- * pointers), UNSUPPORTED_DTYPE or HIP_ERROR.  Enqueued on `stream` (a
+ * pointers, y partly over x or over the weight), UNSUPPORTED_DTYPE or HIP_ERROR.  Enqueued on `stream` (a
  * hipStream_t, NULL = default stream); nothing is allocated and the call does
  * not synchronise.
  */

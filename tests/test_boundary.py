@@ -46,6 +46,9 @@ def test_version(lib):
 BF16, F32, F16 = gm.BF16, gm.F32, gm.F16
 ID, RELU, SILU = gm.EPI_IDENTITY, gm.EPI_RELU, gm.EPI_SILU
 FAKE = 0x10000  # never dereferenced: every call below is rejected before any launch
+# distinct fake operands, 1 TiB apart, for checks that come after the one that
+# rejects operands sharing bytes
+FA, FB, FC, FD = 1 << 40, 2 << 40, 3 << 40, 4 << 40
 
 
 @pytest.mark.parametrize("args,status", [
@@ -295,7 +298,7 @@ def test_grouped_option_checks(lib):
     o.flags = 2
     assert gm.gemm_mkl_grouped(*ok, o) == -6                              # no stream-K
     assert gm.gemm_mkl_grouped(*ok, gm.make_opts(prefetch_stages=-3)) == -1
-    args = (FAKE, FAKE, FAKE, FAKE, 2, 8, 8, 64, BF16, ID, None)
+    args = (FA, FB, FC, FD, 2, 8, 8, 64, BF16, ID, None)
     assert gm.gemm_mkl_grouped(*args, gm.make_opts(config_id=10_000)) == -6  # no such configuration
     f32_ids = [i for i, n in enumerate(gm.config_names()) if n.startswith("f32")]
     assert gm.gemm_mkl_grouped(*args, gm.make_opts(config_id=f32_ids[0])) == -6  # another dtype's
@@ -342,9 +345,9 @@ def test_grouped_config_query(lib):
     ((FAKE, FAKE + 1, FAKE, 4, 64, 1e-6, BF16, -1), -1),            # weight not element-aligned
     ((FAKE, FAKE, FAKE, 4, 64, 1e-6, F32, 99), -1),                 # no such variant
     ((FAKE, FAKE, FAKE, 4, 64, 1e-6, F32, -2), -1),
-    ((FAKE + 4, FAKE, FAKE, 4, 64, 1e-6, F32, 1), -6),              # vector variant, x not 16-byte aligned
-    ((FAKE, FAKE, FAKE, 4, 3, 1e-6, F32, 1), -6),                   # vector variant, row not 16-byte multiple
-    ((FAKE, FAKE, FAKE, 4, 512, 1e-6, F32, 1), -6),                 # vector variant covering 256 floats
+    ((FA + 4, FB, FC, 4, 64, 1e-6, F32, 1), -6),              # vector variant, x not 16-byte aligned
+    ((FA, FB, FC, 4, 3, 1e-6, F32, 1), -6),                   # vector variant, row not 16-byte multiple
+    ((FA, FB, FC, 4, 512, 1e-6, F32, 1), -6),                 # vector variant covering 256 floats
     ((None, None, None, 0, 64, 1e-6, F32, -1), 0),                  # no rows: no launch
     ((None, None, None, 4, 0, 1e-6, BF16, -1), 0),                  # no columns
 ])
@@ -456,7 +459,7 @@ def test_noalloc_argument_checks(lib):
     """gemm_mkl_noalloc's checks run before any HIP call: these calls never
     reach the scratch or a kernel."""
     call = lambda M, N, K, L, dtype, epi, o: lib.gemm_mkl_noalloc(  # noqa: E731
-        FAKE, FAKE, FAKE, M, N, K, L, dtype, epi, None, ctypes.byref(o) if o is not None else None)
+        FA, FB, FC, M, N, K, L, dtype, epi, None, ctypes.byref(o) if o is not None else None)
     # a caller workspace makes no sense here
     assert call(64, 64, 64, 1, BF16, ID, gm.make_opts(workspace_ptr=FAKE, workspace_bytes=1 << 20)) == -1
     # the checks of gemm_mkl_ex, in its order
@@ -507,3 +510,38 @@ def test_workspace_tensor_must_be_on_the_operands_gpu():
         gm._binding._workspace_args(bytearray(64), gpu)
     ptr, nbytes = gm._binding._workspace_args(torch.zeros(64, dtype=torch.float64), torch.device("cpu"))
     assert nbytes == 512 and ptr != 0
+
+
+def test_operands_that_share_bytes_are_rejected(lib):
+    """C is written while A and B are read, so no byte may belong to both; the
+    same holds for a caller workspace, the grouped offsets and the RMSNorm's
+    x (unless y is x itself) and weight.  Every call here is rejected before
+    any HIP call; calls on adjacent, disjoint ranges run in the GPU tests."""
+    M, N, K, L = 64, 48, 32, 2
+    a_bytes, b_bytes, c_bytes = L * M * K * 2, L * N * K * 2, L * M * N * 2
+    ex = lambda A, B, C, opts=None: gm.gemm_mkl_ex(A, B, C, M, N, K, L, BF16, ID, None, opts)  # noqa: E731
+    assert ex(FA, FB, FA) == -1                                   # C is A
+    assert ex(FA, FB, FB + b_bytes - 2) == -1                     # C starts on B's last element
+    assert ex(FA, FB, FA - c_bytes + 2) == -1                     # C ends on A's first element
+    assert ex(FA, FB, FB - 2) == -1                               # C straddles B's start
+    ws = lambda p, n: gm.make_opts(workspace_ptr=p, workspace_bytes=n)  # noqa: E731
+    assert ex(FA, FB, FC, ws(FA + a_bytes - 256, 512)) == -1      # workspace over the end of A
+    assert ex(FA, FB, FC, ws(FC - 256, 512)) == -1                # workspace ending inside C
+    assert ex(FA, FB, FC, ws(FB - (1 << 20), (1 << 20) + 256)) == -1  # workspace running into B
+    # the raw entry point and the no-allocation one check the same
+    assert gm.gemm_mkl(FA, FB, FB, M, N, K, L, BF16, ID, None) == -1
+    assert lib.gemm_mkl_noalloc(FA, FB, FA + 64, M, N, K, L, BF16, ID, None, None) == -1
+    # grouped: C against A, B, offsets; the workspace against all four
+    G, T = 3, 40
+    g = lambda A, B, C, offs, opts=None: gm.gemm_mkl_grouped(A, B, C, offs, G, T, N, K, BF16, ID, None, opts)  # noqa: E731
+    assert g(FA, FB, FA + 2, FD) == -1
+    assert g(FA, FB, FB, FD) == -1
+    assert g(FA, FB, FC, FC + T * N * 2 - 4) == -1                # offsets on C's last bytes
+    assert g(FA, FB, FC, FD, ws(FD - 256, 512)) == -1             # workspace over the offsets
+    assert g(FA, FB, FC, FD, ws(FC + 256, 256)) == -1             # workspace inside C
+    # RMSNorm: y partly over x, or over the weight
+    rows, H = 8, 64
+    rms = lambda x, w, y: gm.gemm_mkl_rms_norm(x, w, y, rows, H, 1e-6, F32, None)  # noqa: E731
+    assert rms(FA, FB, FA + 4 * H) == -1                          # y one row past x: rows overlap
+    assert rms(FA + 4, FB, FA) == -1
+    assert rms(FA, FC + 4 * H, FC) == -1                          # the weight inside y

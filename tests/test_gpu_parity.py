@@ -243,6 +243,31 @@ def test_guard_bands_untouched(dtype):
     assert_bits_equal(workloads.torch_to_storage(out), workloads.torch_to_storage(ref), "caller vs internal workspace")
 
 
+def test_operands_end_to_end_in_one_buffer():
+    """A, B and C laid end to end in one allocation share no byte: the call
+    runs and equals the call on separate tensors bit for bit.  A C over A is
+    refused (INVALID_VALUE) before any launch, and A is left as it was."""
+    import torch
+
+    M, N, K, L = 96, 80, 128, 2
+    A, B = _operands("bf16", M, N, K, L, seed=21)
+    a, b = to_device(A, "bf16"), to_device(B, "bf16")
+    na, nb, nc = a.numel(), b.numel(), L * M * N
+    buf = torch.empty(na + nb + nc, dtype=a.dtype, device=a.device)
+    buf[:na] = a.flatten()
+    buf[na:na + nb] = b.flatten()
+    a2, b2, c2 = buf[:na].view(L, M, K), buf[na:na + nb].view(L, N, K), buf[na + nb:].view(L, M, N)
+    gm.gemm(a2, b2, "relu", out=c2)
+    ref = gm.gemm(a, b, "relu")
+    torch.cuda.synchronize()
+    assert_bits_equal(workloads.torch_to_storage(c2), workloads.torch_to_storage(ref), "one buffer vs separate")
+    with pytest.raises(gm.GemmMklError) as e:
+        gm.gemm(a2, b2, "relu", out=buf[:nc].view(L, M, N))
+    assert e.value.status == -1
+    torch.cuda.synchronize()
+    assert torch.equal(a2, a)
+
+
 def test_workspace_too_small_is_rejected_and_C_untouched():
     import torch
 

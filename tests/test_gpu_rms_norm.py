@@ -182,3 +182,27 @@ def test_rms_norm_empty():
     assert gm.rms_norm(x).shape == (0, 64)
     x = torch.empty((5, 0), device="cuda", dtype=torch.bfloat16)
     assert gm.rms_norm(x).shape == (5, 0)
+
+
+def test_rms_norm_partial_overlap_is_refused():
+    """y may be x itself, but an output that starts one row into x (or lies
+    over the weight) is refused before any launch, and x is left as it was."""
+    import torch
+
+    rows, hidden = 16, 256
+    buf = torch.randn(rows * hidden + hidden, device="cuda")
+    x = buf[:rows * hidden].view(rows, hidden)
+    before = x.clone()
+    with pytest.raises(gm.GemmMklError) as e:
+        gm.rms_norm(x, out=buf[hidden:].view(rows, hidden))
+    assert e.value.status == -1
+    w = torch.ones(hidden, device="cuda")
+    y = torch.empty(rows, hidden, device="cuda")
+    with pytest.raises(gm.GemmMklError) as e:
+        gm.rms_norm(x, y[1], out=y)
+    assert e.value.status == -1
+    torch.cuda.synchronize()
+    assert torch.equal(x, before)
+    xi = x.clone()
+    gm.rms_norm(xi, w, out=xi)   # in place stays allowed
+    assert torch.equal(gm.rms_norm(x, w), xi)

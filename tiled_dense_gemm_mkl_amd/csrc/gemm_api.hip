@@ -116,6 +116,16 @@ bool mul_ok(int64_t a, int64_t b, int64_t *out)
     return true;
 }
 
+// True when the byte ranges [p, p + pn) and [q, q + qn) share a byte (no end
+// address is formed, so ranges near the top of the address space compare
+// correctly).
+bool overlaps(const void *p, uint64_t pn, const void *q, uint64_t qn)
+{
+    if (pn == 0 || qn == 0) return false;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+    return a <= b ? b - a < pn : a - b < qn;
+}
+
 struct Plan {
     int config_id = -1;
     int P = 0;
@@ -740,6 +750,21 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
     const int es = elem_bytes(dtype);
     auto al = [](const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; };
     if (!al(A, es) || !al(B, es) || !al(C, es)) return GEMM_MKL_STATUS_INVALID_VALUE;
+    // C is written while A and B are read, and a caller workspace takes
+    // partial sums or repacked operands while all three are in use: ranges
+    // that share a byte would feed results back into the sums.  (The sizes
+    // were checked for overflow above.)
+    {
+        const uint64_t a_bytes = K > 0 ? uint64_t(L * M * K * es) : 0, b_bytes = K > 0 ? uint64_t(L * N * K * es) : 0;
+        const uint64_t c_bytes = uint64_t(L * M * N * es);
+        if (overlaps(C, c_bytes, A, a_bytes) || overlaps(C, c_bytes, B, b_bytes)) return GEMM_MKL_STATUS_INVALID_VALUE;
+        if (o && o->workspace) {
+            const uint64_t w = o->workspace_bytes;
+            if (overlaps(o->workspace, w, A, a_bytes) || overlaps(o->workspace, w, B, b_bytes) ||
+                overlaps(o->workspace, w, C, c_bytes))
+                return GEMM_MKL_STATUS_INVALID_VALUE;
+        }
+    }
     const int align = (al(A, 16) ? kAlignA : 0) | (al(B, 16) ? kAlignB : 0) | (al(C, 4 * es) ? kAlignC : 0);
 
     Plan plan;
@@ -923,6 +948,20 @@ int run_grouped(const void *A, const void *B, void *C, const int32_t *offs, int6
     if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_MKL_STATUS_INVALID_VALUE;
     auto al = [](const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; };
     if (!al(A, es) || !al(B, es) || !al(C, es) || !al(offs, 4)) return GEMM_MKL_STATUS_INVALID_VALUE;
+    // C is written while A, B and the offsets are read (and a caller
+    // workspace takes the repacked operands): no two may share a byte.
+    {
+        const uint64_t a_bytes = K > 0 ? uint64_t(total_m * K * es) : 0, b_bytes = K > 0 ? uint64_t(G * N * K * es) : 0;
+        const uint64_t c_bytes = uint64_t(total_m * N * es), o_bytes = uint64_t(G) * 4;
+        if (overlaps(C, c_bytes, A, a_bytes) || overlaps(C, c_bytes, B, b_bytes) || overlaps(C, c_bytes, offs, o_bytes))
+            return GEMM_MKL_STATUS_INVALID_VALUE;
+        if (o && o->workspace) {
+            const uint64_t w = o->workspace_bytes;
+            if (overlaps(o->workspace, w, A, a_bytes) || overlaps(o->workspace, w, B, b_bytes) ||
+                overlaps(o->workspace, w, C, c_bytes) || overlaps(o->workspace, w, offs, o_bytes))
+                return GEMM_MKL_STATUS_INVALID_VALUE;
+        }
+    }
     // The tiled kernels read 16-byte pieces: rows of K elements that are not
     // a multiple of 16 bytes, or an A or B off a 16-byte boundary, are first
     // copied into zero-padded rows of Kp elements in the workspace (the zeros

@@ -301,6 +301,14 @@ int choose(int64_t H, int dtype, bool vec_ok)
     return 0;
 }
 
+// True when the byte ranges [p, p + pn) and [q, q + qn) share a byte.
+bool byte_overlap(const void *p, uint64_t pn, const void *q, uint64_t qn)
+{
+    if (pn == 0 || qn == 0) return false;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+    return a <= b ? b - a < pn : a - b < qn;
+}
+
 int check(const void *x, const void *weight, const void *y, int64_t rows, int64_t H, float eps, int dtype,
           int variant, bool *vec_ok)
 {
@@ -314,6 +322,13 @@ int check(const void *x, const void *weight, const void *y, int64_t rows, int64_
     if (rows > 0 && H > 0) {
         if (x == nullptr || y == nullptr) return GEMM_MKL_STATUS_INVALID_VALUE;
         if (!al(x, es) || !al(y, es) || !al(weight, es)) return GEMM_MKL_STATUS_INVALID_VALUE;
+        // y may be x itself: a row's sum of squares is complete before any
+        // of the row is written, and each element is then read by the thread
+        // that overwrites it.  Any other byte that y shares with x or the
+        // weight would let one row's output change another row's input.
+        const uint64_t n = uint64_t(rows * H * es), wn = weight ? uint64_t(H * es) : 0;
+        if ((y != x && byte_overlap(y, n, x, n)) || byte_overlap(y, n, weight, wn))
+            return GEMM_MKL_STATUS_INVALID_VALUE;
     }
     *vec_ok = al(x, 16) && al(y, 16) && al(weight, 16) && (H * es) % 16 == 0;
     return GEMM_MKL_STATUS_OK;
