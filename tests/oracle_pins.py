@@ -193,6 +193,49 @@ def check_epilogue_values(lib):
         assert abs(d - x) <= 8 * np.spacing(max(abs(x), abs(s))), "silu(x) - silu(-x) = x"
 
 
+def check_special_values(lib):
+    """IEEE special values through the epilogues, the sum and the rounding:
+    closed forms of binary64 arithmetic (inf * 0 and inf - inf are NaN, an
+    infinite term dominates every finite one) and of the readings (ReLU is
+    where(x > 0, x, 0), so NaN and -inf give +0; SiLU is x / (1 + exp(-x)),
+    so +inf gives +inf and -inf gives -inf / inf = NaN)."""
+    inf, nan = math.inf, math.nan
+    ep = lambda x, e: oracle.epilogue64(x, e, lib)  # noqa: E731
+    for e in EPIS:
+        assert math.isnan(ep(nan, e)) == (e != "relu"), f"{e}(NaN)"
+    for x, want in ((nan, 0.0), (inf, inf), (-inf, 0.0)):
+        v = ep(x, "relu")
+        assert v == want and math.copysign(1.0, v) == 1.0, f"relu({x}) = {v}"
+    assert ep(inf, "silu") == inf and math.isnan(ep(-inf, "silu"))
+    assert ep(inf, "identity") == inf and ep(-inf, "identity") == -inf
+    for dtype in DTYPES:
+        # rows of A: +inf at k=1; +inf at k=1 and -inf at k=2; NaN at k=3; ones
+        # rows of B: ones; ones with 0 at k=1; minus ones
+        Av = np.ones((1, 4, 5))
+        Av[0, 0, 1] = inf
+        Av[0, 1, 1], Av[0, 1, 2] = inf, -inf
+        Av[0, 2, 3] = nan
+        Bv = np.ones((1, 3, 5))
+        Bv[0, 1, 1] = 0.0
+        Bv[0, 2, :] = -1.0
+        to_bits = {"f32": lambda v: v.astype(np.float32),
+                   "f16": lambda v: v.astype(np.float16).view(np.uint16),
+                   "bf16": lambda v: (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)}[dtype]
+        C = oracle.gemm64(to_bits(Av), to_bits(Bv), dtype, "identity", lib=lib)
+        want = np.array([[inf, nan, -inf], [nan, nan, nan], [nan, nan, nan], [5.0, 4.0, -5.0]])
+        assert np.array_equal(np.isnan(C[0]), np.isnan(want)), f"{dtype}: NaN pattern {C[0]}"
+        fin = ~np.isnan(want)
+        assert np.array_equal(C[0][fin], want[fin]), f"{dtype}: {C[0]}"
+        R = oracle.gemm64(to_bits(Av), to_bits(Bv), dtype, "relu", lib=lib)[0]
+        assert np.array_equal(R, np.where(want > 0, want, 0.0)) and not np.any(np.signbit(R)), f"{dtype}: relu {R}"
+        # rounding keeps infinities and NaN; the largest finite value times 2 overflows
+        big = {"f32": float(np.finfo(np.float32).max), "f16": 65504.0, "bf16": float(np.array([0x7F7F0000], np.uint32).view(np.float32)[0])}[dtype]
+        bits = oracle.round_to_dtype(np.array([inf, -inf, nan, 2 * big, -2 * big]), dtype, lib)
+        back = _exact_values(bits, dtype)
+        assert back[0] == inf and back[1] == -inf and math.isnan(back[2]), f"{dtype}: {back}"
+        assert back[3] == inf and back[4] == -inf, f"{dtype}: overflow {back}"
+
+
 # ------------------------------------------------------------------ GEMM pins
 
 def check_closed_form_identity_B(lib):
@@ -449,6 +492,7 @@ ALL_CHECKS = [
     check_round_f16_vs_numpy,
     check_round_f32_vs_cast,
     check_epilogue_values,
+    check_special_values,
     check_closed_form_identity_B,
     check_closed_form_all_ones,
     check_bruteforce_fraction,

@@ -36,6 +36,10 @@ MUTANTS = [
      "widen(B, dtype, (b_off / K) + k)", ["check_bruteforce_fraction"]),
     ("ReLU keeps -0", "return (x > 0.0) ? x : 0.0;", "return (x >= 0.0) ? x : 0.0;",
      ["check_epilogue_values"]),
+    ("ReLU passes NaN through", "return (x > 0.0) ? x : 0.0;", "return (x <= 0.0) ? 0.0 : x;",
+     ["check_special_values"]),
+    ("fp16 infinity encoded as the largest finite value", "if (isinf(a)) return sign | 0x7c00;",
+     "if (isinf(a)) return sign | 0x7bff;", ["check_special_values"]),
     ("SiLU with the wrong sign in exp", "return x / (1.0 + exp(-x));",
      "return x / (1.0 + exp(x));", ["check_epilogue_values"]),
     ("fp16 subnormal scale off by one", "ldexp((double)f, -24)", "ldexp((double)f, -25)",
