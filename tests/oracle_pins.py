@@ -234,6 +234,14 @@ def check_special_values(lib):
         back = _exact_values(bits, dtype)
         assert back[0] == inf and back[1] == -inf and math.isnan(back[2]), f"{dtype}: {back}"
         assert back[3] == inf and back[4] == -inf, f"{dtype}: overflow {back}"
+        # RMSNorm: a row with an infinity has an infinite sum of squares, so
+        # its scale 1/sqrt(inf) is 0: inf * 0 is NaN, finite elements become
+        # signed zeros; a NaN anywhere in a row makes the whole row NaN
+        x = to_bits(np.array([[inf, 1.0, -2.0], [1.0, nan, 1.0], [-inf, -inf, 3.0]]))
+        y = oracle.rms_norm64(x, to_bits(np.ones(3)), 1e-6, dtype, lib=lib)
+        assert math.isnan(y[0, 0]) and y[0, 1] == 0.0 and not np.signbit(y[0, 1]), f"{dtype}: {y[0]}"
+        assert y[0, 2] == 0.0 and np.signbit(y[0, 2]), f"{dtype}: -2 * 0 is -0 ({y[0]})"
+        assert np.isnan(y[1]).all() and np.isnan(y[2, :2]).all() and y[2, 2] == 0.0, f"{dtype}: {y[1:]}"
 
 
 # ------------------------------------------------------------------ GEMM pins

@@ -224,3 +224,32 @@ def test_grouped_many_groups_take_the_remapped_grid(orc):
     Ai, Bi = _operands(dtype, total_m, G, N, K, seed=33, integer=True)
     refi = orc.round_to_dtype(orc.gemm_grouped64(Ai, Bi, offs, dtype, "identity"), dtype)
     assert_bits_equal(_run(Ai, Bi, offs, dtype, "identity"), refi, "700 groups integer")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_grouped_special_values(orc, dtype):
+    """+inf, -inf and NaN planted in A rows of three groups (one of them a
+    one-row group) and in the last k of one column of a fourth group's B, on
+    integer inputs: NaN exactly where the oracle has NaN, every other output
+    of the grouped rows bit for bit, rows in no group untouched."""
+    sizes = [0, 37, 130, 1, 64]
+    G, N, K = len(sizes), 96, 136
+    offs = np.cumsum(sizes).astype(np.int32)
+    total_m = int(offs[-1]) + 2
+    A, B = _operands(dtype, total_m, G, N, K, seed=91, integer=True)
+    Av, Bv = widen_bits(A, dtype), widen_bits(B, dtype)
+    Av[3, 0] = np.inf                 # group 1
+    Av[40, 100] = -np.inf             # group 2
+    Av[167, 5] = np.nan               # group 3, its only row
+    Bv[4, 17, K - 1] = np.inf         # group 4, column 17
+    A, B = workloads.to_storage(Av, dtype), workloads.to_storage(Bv, dtype)
+    rows = np.arange(total_m) < offs[-1]
+    for epi in ("identity", "relu"):
+        C = _run(A, B, offs, dtype, epi)
+        assert np.all(C[~rows] == SENTINEL[dtype]), f"{dtype} {epi}: rows outside every group were written"
+        want64 = orc.gemm_grouped64(A, B, offs, dtype, epi)[rows]
+        got = widen_bits(C[rows], dtype)
+        assert np.array_equal(np.isnan(got), np.isnan(want64)), f"{dtype} {epi}: NaN pattern"
+        num = ~np.isnan(want64)
+        assert_bits_equal(C[rows][num], orc.round_to_dtype(want64, dtype)[num], f"{dtype} {epi}")
+        assert np.isinf(want64).any() and (epi == "relu" or np.isnan(want64).any())

@@ -206,3 +206,33 @@ def test_rms_norm_partial_overlap_is_refused():
     xi = x.clone()
     gm.rms_norm(xi, w, out=xi)   # in place stays allowed
     assert torch.equal(gm.rms_norm(x, w), xi)
+
+
+@pytest.mark.parametrize("hidden", (256, 301))
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_rms_norm_special_values(orc, dtype, hidden):
+    """Rows holding +inf, -inf or NaN, and an all-zero row, through the vector
+    (256) and the general (301) kernel.  A row with an infinity has an
+    infinite sum of squares, so its scale is 0: the infinite element becomes
+    NaN (inf * 0) and every other element a signed zero, on both sides.  A
+    NaN row is all NaN; a zero row stays zero (the scale is 1/sqrt(eps)).
+    The special rows must match the oracle's rounding bit for bit (NaN as a
+    pattern), the ordinary rows within the tolerance."""
+    rng = np.random.default_rng(90)
+    x = rng.standard_normal((6, hidden))
+    x[1, 5] = np.inf
+    x[2, hidden - 1] = -np.inf
+    x[3, 7] = np.nan
+    x[4, :] = 0.0
+    w = 1.0 + 0.5 * rng.standard_normal(hidden)
+    X, W = workloads.to_storage(x, dtype), workloads.to_storage(w, dtype)
+    Y = _run(X, W, dtype)
+    y64 = orc.rms_norm64(X, W, EPS, dtype)
+    got = widen_bits(Y, dtype)
+    assert np.array_equal(np.isnan(got), np.isnan(y64)), "NaN pattern"
+    assert np.isnan(y64[1, 5]) and np.isnan(y64[2, hidden - 1]) and np.isnan(y64[3]).all()
+    special = np.array([1, 2, 3, 4])
+    ref = orc.round_to_dtype(y64[special], dtype)
+    num = ~np.isnan(y64[special])
+    assert_bits_equal(Y[special][num], ref[num], f"{dtype} H={hidden} special rows")
+    _check(Y[[0, 5]], y64[[0, 5]], dtype, f"{dtype} H={hidden} ordinary rows")

@@ -51,7 +51,16 @@ template <> struct Cvt<__bf16> {
 };
 template <> struct Cvt<_Float16> {
     __device__ static __forceinline__ float to(_Float16 v) { return (float)v; }
-    __device__ static __forceinline__ _Float16 from(float v) { return (_Float16)v; }   // RNE
+    __device__ static __forceinline__ _Float16 from(float v)   // RNE
+    {
+        // Left visible, a product followed by this conversion is fused into
+        // one mixed-precision multiply-add whose addend is +0, and a product
+        // of -0 then comes out as +0.  The empty asm hands the conversion an
+        // opaque fp32 value, so the product is rounded to fp32 and converted
+        // with its sign.
+        asm("" : "+v"(v));
+        return (_Float16)v;
+    }
 };
 
 // Sum over the 64 lanes of a wave, every lane ending with the same bits:
