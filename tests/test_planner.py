@@ -121,3 +121,33 @@ def test_16bit_fixup_only_when_forced():
         assert _plan(M, N, K, 1, "bf16")["fixup"] == 0
     assert _plan(512, 5632, 2048, 1, "bf16", split_k=2, fixup=True)["fixup"] == 1
     assert _plan(512, 5632, 2048, 1, "bf16", split_k=2)["fixup"] == 1
+
+
+def test_long_rows_stay_inside_one_buffer_descriptor():
+    """A tile kernel addresses a tile's rows of A and B through one buffer
+    descriptor whose offsets are below 2^31: for every K the plan's tile must
+    span fewer bytes than that (with a row of slack), a forced configuration
+    that would not is NOT_AVAILABLE, and rows too long for every tile take the
+    general kernel, which indexes with 64-bit pointers, without repacking."""
+    names = gm.config_names()
+    for dtype, es in ((gm.BF16, 2), (gm.F32, 4)):
+        for K in (2 ** 20, 2 ** 21, 2 ** 22, 2 ** 23, 2 ** 24, 2 ** 26, 2 ** 26 + 1, 2 ** 30 + 3):
+            p = gm.get_plan(512, 512, K, 1, dtype, gm.EPI_RELU)
+            if p["general"]:
+                assert p["packed"] == 0 and p["split_k"] == 1
+                continue
+            assert (max(p["block_m"], p["block_n"]) + 1) * K * es < 2 ** 31, (dtype, K, p)
+        for cid, name in enumerate(names):
+            if not name.startswith("bf16" if dtype == gm.BF16 else "f32"):
+                continue
+            bm, bn = (int(x) for x in name.split()[1].split("x"))
+            span = (max(bm, bn) + 1) * es
+            # the tile's rows just below 2^31 bytes: the forced configuration runs
+            K = (2 ** 31 - 65536) // span // 64 * 64
+            assert gm.get_plan(512, 512, K, 1, dtype, gm.EPI_RELU, gm.make_opts(config_id=cid))["config_id"] == cid
+            K = 2 ** 31 // span // 64 * 64 + 64   # just past: refused
+            with pytest.raises(gm.GemmMklError) as e:
+                gm.get_plan(512, 512, K, 1, dtype, gm.EPI_RELU, gm.make_opts(config_id=cid))
+            assert e.value.status == -6, (name, K)
+    # the largest K is planned on the general kernel, never packed
+    assert gm.get_plan(4, 4, 2 ** 30 + 3, 1, gm.BF16, gm.EPI_IDENTITY)["general"] == 1
