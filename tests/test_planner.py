@@ -151,3 +151,18 @@ def test_long_rows_stay_inside_one_buffer_descriptor():
             assert e.value.status == -6, (name, K)
     # the largest K is planned on the general kernel, never packed
     assert gm.get_plan(4, 4, 2 ** 30 + 3, 1, gm.BF16, gm.EPI_IDENTITY)["general"] == 1
+
+
+def test_grouped_long_rows_fit_one_descriptor_or_are_refused():
+    """The grouped kernels address a tile's rows the same way: the chosen
+    configuration's tile spans less than 2^31 bytes of rows, and rows too long
+    for every grouped configuration are NOT_AVAILABLE (there is no general
+    grouped kernel) rather than planned past the range."""
+    names = gm.config_names()
+    for K in (2 ** 20, 2 ** 22, 2 ** 23):
+        cid = gm.grouped_config(4, 512, 256, K, gm.BF16, gm.EPI_RELU)
+        bm, bn = (int(x) for x in names[cid].split()[1].split("x"))
+        assert (max(bm, bn) + 1) * K * 2 < 2 ** 31, (K, names[cid])
+    with pytest.raises(gm.GemmMklError) as e:
+        gm.grouped_config(4, 512, 256, 2 ** 25, gm.BF16, gm.EPI_RELU)
+    assert e.value.status == -6
