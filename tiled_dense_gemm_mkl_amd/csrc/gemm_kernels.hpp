@@ -1837,9 +1837,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 // A row starts `lead` bytes (0, or 2 for a 16-bit row) past a 4-byte
 // boundary: each piece is read as 20 bytes from that boundary (a 16-byte and
 // a 4-byte buffer load, dword-aligned) and shifted into place with
-// v_alignbyte.  A load that reaches past the operand's last byte would come
+// v_alignbyte.  A load that reaches past the operand's last byte, or past
+// the descriptor's range (2^31 - 1 bytes from the row's start), would come
 // back zeroed by the buffer's range check, valid bytes included, so the
-// pieces whose 20 bytes do not all lie in the operand (the last one or two of
+// pieces whose 20 bytes do not all lie inside both (the last one or two of
 // the last row) are read element by element instead.  The 4-byte word a row
 // starts in lies in the operand's allocation.
 template <class T>
@@ -1854,15 +1855,17 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const T *__restrict__ sr
         const uintptr_t base = row0 & ~(uintptr_t)3;
         const uint32_t lead = (uint32_t)(row0 - base);
         const uint64_t avail = end - base;
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            reinterpret_cast<void *>(base), (short)0, (int)(avail < 0x7fffffffu ? avail : 0x7fffffffu), 0x00020000);
+        const uint64_t lim = avail < 0x7fffffffu ? avail : 0x7fffffffu;   // the descriptor's range
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(base), (short)0, (int)lim, 0x00020000);
         T *d = dst + r * Kp;
         const T *s = src + r * K;
         for (int64_t v = threadIdx.x; v < vpr; v += 256) {
-            const int off = (int)(v * 16);
+            const uint64_t off64 = (uint64_t)v * 16;
+            const int off = (int)off64;   // below 2^31 wherever it is used
             const int64_t k0 = v * V;
             i32x4 w;
-            if ((uint64_t)off + 20 <= avail) {
+            if (off64 + 20 <= lim) {
                 const i32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
                 const int hi = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 16, 0, 0);
                 w = lo;
